@@ -1,0 +1,277 @@
+/*
+ * qsa_oracle.c — plain CPU oracle of one Qwen Sparse Attention layer step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this code.  It shares nothing
+ * with the HIP library (no header, helper, table or constant) and the
+ * library never calls it.
+ *
+ * Everything is computed with straightforward loops in fp64 from the exact
+ * values of the stored inputs, in the order the method is described:
+ *   indexer score -> exact top-K -> expansion to tokens -> attention.
+ * Sources (page title, section):
+ *   - "Qwen3.8-27B QSA - BF16 source weights", "QSA in brief": selection in
+ *     4-token blocks by a learned compressed indexer, fixed K plus the
+ *     current block, all KV retained.
+ *   - TensorRT-LLM "QSASparseAttentionConfig": exact radix top-K over the
+ *     compressed groups (enable_heuristic_topk), token-granular expanded
+ *     selections (get_indices_block_size), selection sharing in the MTP
+ *     draft loop with appended completed groups
+ *     (index_share_for_mtp_iteration).
+ *   - OrcaRouter article on SGLang PR #41855, "Neun bestandene Tests ...":
+ *     -1 padded selections, zero output for rows that select nothing,
+ *     causal tail of 0..3 tokens at ratio 4.
+ * Readings where the pages are silent (the indexer formula, the tie order,
+ * the FP8 flavour) are listed in the design notes and restated at each
+ * function below.
+ *
+ * Pins: every function here is checked by tests against facts that do not
+ * come from this file (format definitions, closed forms, brute force,
+ * torch's CPU attention, invariants).  The indexer formula itself is an
+ * assumed form: its pins check the code against that form, not against the
+ * pages, which do not print it.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------------- */
+/* Exact values of stored elements                                        */
+/* ---------------------------------------------------------------------- */
+
+/* OCP 8-bit E4M3FN (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * exponent field 0 is subnormal with weight 2^-6; field 15 with mantissa 7
+ * is NaN; there is no infinity; largest finite 448). */
+double qo_fp8_e4m3(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, -6);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* bfloat16: the upper half of an IEEE binary32. */
+double qo_bf16(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* Round a binary32 to the nearest bfloat16 value, ties to even (used for
+ * the prefill indexer, which multiplies bf16 operands). */
+float qo_round_bf16(float x) {
+  if (x != x) return x;
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  uint32_t lsb = (u >> 16) & 1u;
+  u = (u + 0x7FFFu + lsb) & 0xFFFF0000u;
+  float r;
+  memcpy(&r, &u, 4);
+  return r;
+}
+
+static double kv_value(const void* cache, int kv_dtype, int64_t index) {
+  if (kv_dtype == 0) return qo_bf16(((const uint16_t*)cache)[index]);
+  return qo_fp8_e4m3(((const uint8_t*)cache)[index]);
+}
+
+static int page_ok(int32_t p, int num_pages) { return p >= 0 && p < num_pages; }
+
+/* ---------------------------------------------------------------------- */
+/* Step 1: indexer scores                                                 */
+/* ---------------------------------------------------------------------- */
+
+/* score[g] = sum_h w[h] * max(0, sum_d q[h][d] * khat[g][h][d]) for every
+ * complete group g < floor(L/ratio) of the row; -inf for g >= floor(L/ratio)
+ * and for groups whose page id is out of range.  The form is the assumed
+ * per-head ReLU-weighted indexer (the pages do not print one).
+ * Products of two binary32 values are exact in binary64 and the sums run in
+ * binary64, so the single final rounding to binary32 gives (up to a
+ * double-rounding tie) the correctly rounded score.  With round_bf16 != 0
+ * q and khat are first rounded to bf16 (prefill precision).
+ * gstride is the row stride of `out`; columns >= floor(L/ratio) up to
+ * gstride are set to -inf.  Rows whose L is outside [0, gstride*ratio]
+ * get all -inf. */
+void qo_scores(int n_rows, const int32_t* row_req, const int32_t* row_len, int Hi, int Di,
+               int page, int ratio, const float* q_idx, const float* w_idx, const float* khat,
+               const int32_t* page_table, int max_pages, int num_pages, int round_bf16,
+               int gstride, float* out) {
+  int gpp = page / ratio; /* groups per page */
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int r = 0; r < n_rows; ++r) {
+    int L = row_len[r];
+    int G = (L >= 0 && L <= gstride * ratio) ? L / ratio : 0;
+    const float* q = q_idx + (int64_t)r * Hi * Di;
+    const float* w = w_idx + (int64_t)r * Hi;
+    float* o = out + (int64_t)r * gstride;
+    for (int g = 0; g < gstride; ++g) o[g] = -INFINITY;
+    for (int g = 0; g < G; ++g) {
+      int32_t phys = page_table[(int64_t)row_req[r] * max_pages + g / gpp];
+      if (!page_ok(phys, num_pages)) continue;
+      const float* kg = khat + ((int64_t)phys * gpp + g % gpp) * Hi * Di;
+      double s = 0.0;
+      for (int h = 0; h < Hi; ++h) {
+        double a = 0.0;
+        for (int d = 0; d < Di; ++d) {
+          float qv = q[h * Di + d], kv = kg[h * Di + d];
+          if (round_bf16) { qv = qo_round_bf16(qv); kv = qo_round_bf16(kv); }
+          a += (double)qv * (double)kv;
+        }
+        s += (double)w[h] * (a > 0.0 ? a : 0.0);
+      }
+      float s32 = (float)s;
+      if (s32 == 0.0f) s32 = 0.0f; /* -0 -> +0 */
+      o[g] = s32;
+    }
+  }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Step 2: exact top-K                                                    */
+/* ---------------------------------------------------------------------- */
+
+typedef struct { float s; int32_t g; } scored;
+
+/* Total order of the selection: higher score first; equal scores (+0 and
+ * -0 compare equal) go to the lower group index.  The pages do not state a
+ * tie rule; lowest index first is the reading taken. */
+static int by_rank(const void* a, const void* b) {
+  const scored* x = (const scored*)a;
+  const scored* y = (const scored*)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return (x->g > y->g) - (x->g < y->g);
+}
+
+static int ascending(const void* a, const void* b) {
+  int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+/* For each row keep min(K, G) groups among g < G (G = row_G[r]): all of
+ * them if G <= K, else the first K in the total order above.  Output is
+ * ascending group ids padded with -1 to K entries.  Returns the number of
+ * NaN scores met among candidates (NaN has no place in the order; callers
+ * treat a nonzero return as an error). */
+int qo_topk(int n_rows, const int32_t* row_G, int K, const float* scores, int gstride,
+            int32_t* out) {
+  int nan_count = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : nan_count)
+  for (int r = 0; r < n_rows; ++r) {
+    int G = row_G[r] < 0 ? 0 : (row_G[r] > gstride ? gstride : row_G[r]);
+    const float* s = scores + (int64_t)r * gstride;
+    int32_t* o = out + (int64_t)r * K;
+    for (int i = 0; i < K; ++i) o[i] = -1;
+    for (int g = 0; g < G; ++g) nan_count += (s[g] != s[g]);
+    if (G <= K) {
+      for (int g = 0; g < G; ++g) o[g] = g;
+      continue;
+    }
+    scored* all = (scored*)malloc(sizeof(scored) * (size_t)G);
+    for (int g = 0; g < G; ++g) { all[g].s = s[g]; all[g].g = g; }
+    qsort(all, (size_t)G, sizeof(scored), by_rank);
+    for (int i = 0; i < K; ++i) o[i] = all[i].g;
+    qsort(o, (size_t)K, sizeof(int32_t), ascending);
+    free(all);
+  }
+  return nan_count;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Step 3: expansion                                                      */
+/* ---------------------------------------------------------------------- */
+
+/* Token list of one query row: tokens ratio*g .. ratio*g+ratio-1 of every
+ * selected group (ascending input, -1 entries ignored), followed by the
+ * contiguous range [tail_begin, tail_end) (the current partial block, plus
+ * any groups completed by draft positions).  Written ascending into
+ * out[0..width), padded with -1.  Returns the count, or -1 if it exceeds
+ * width. */
+int qo_expand(int K, const int32_t* groups, int ratio, int tail_begin, int tail_end, int width,
+              int32_t* out) {
+  int n = 0;
+  for (int i = 0; i < width; ++i) out[i] = -1;
+  for (int i = 0; i < K; ++i) {
+    if (groups[i] < 0) continue;
+    for (int j = 0; j < ratio; ++j) {
+      if (n >= width) return -1;
+      out[n++] = groups[i] * ratio + j;
+    }
+  }
+  for (int t = tail_begin; t < tail_end; ++t) {
+    if (n >= width) return -1;
+    out[n++] = t;
+  }
+  qsort(out, (size_t)n, sizeof(int32_t), ascending);
+  return n;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Step 4: attention over a token list                                    */
+/* ---------------------------------------------------------------------- */
+
+/* For each query row r (page-table row row_req[r], token list
+ * tokens[r*width .. ], -1 entries ignored) and query head h, with KV head
+ * kh = h / (Hq / Hkv):
+ *   z_t = sm_scale * sum_d q[r,h,d] * K[t,kh,d] * k_scale
+ *   out[r,h,:] = sum_t exp(z_t - max z) * V[t,kh,:] * v_scale / sum_t exp(z_t - max z)
+ * in binary64.  Tokens on out-of-range pages are skipped; a row with no
+ * token gives exact zeros. */
+void qo_attend(int n_rows, const int32_t* row_req, const int32_t* tokens, int width, int Hq,
+               int Hkv, int D, int page, int kv_dtype, const void* k_cache, const void* v_cache,
+               double k_scale, double v_scale, double sm_scale, const int32_t* page_table,
+               int max_pages, int num_pages, const uint16_t* q, double* out) {
+  int group = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int r = 0; r < n_rows; ++r) {
+    for (int h = 0; h < Hq; ++h) {
+      int kh = h / group;
+      const int32_t* tl = tokens + (int64_t)r * width;
+      const uint16_t* qh = q + ((int64_t)r * Hq + h) * D;
+      double* o = out + ((int64_t)r * Hq + h) * D;
+      double* z = (double*)malloc(sizeof(double) * (size_t)(width > 0 ? width : 1));
+      int64_t* base = (int64_t*)malloc(sizeof(int64_t) * (size_t)(width > 0 ? width : 1));
+      int n = 0;
+      double zmax = -INFINITY;
+      for (int i = 0; i < width; ++i) {
+        int32_t t = tl[i];
+        if (t < 0) continue;
+        int32_t phys = page_table[(int64_t)row_req[r] * max_pages + t / page];
+        if (!page_ok(phys, num_pages)) continue;
+        int64_t b0 = (((int64_t)phys * page + t % page) * Hkv + kh) * D;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += qo_bf16(qh[d]) * (kv_value(k_cache, kv_dtype, b0 + d) * k_scale);
+        z[n] = sm_scale * dot;
+        base[n] = b0;
+        if (z[n] > zmax) zmax = z[n];
+        ++n;
+      }
+      for (int d = 0; d < D; ++d) o[d] = 0.0;
+      if (n > 0) {
+        double denom = 0.0;
+        for (int i = 0; i < n; ++i) {
+          double p = exp(z[i] - zmax);
+          denom += p;
+          for (int d = 0; d < D; ++d) o[d] += p * (kv_value(v_cache, kv_dtype, base[i] + d) * v_scale);
+        }
+        for (int d = 0; d < D; ++d) o[d] /= denom;
+      }
+      free(z);
+      free(base);
+    }
+  }
+}
+
+int qo_num_threads(void) {
+#ifdef _OPENMP
+  extern int omp_get_max_threads(void);
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
