@@ -95,8 +95,8 @@ static int page_ok(int32_t p, int num_pages) { return p >= 0 && p < num_pages; }
  * double-rounding tie) the correctly rounded score.  With round_bf16 != 0
  * q and khat are first rounded to bf16 (prefill precision).
  * gstride is the row stride of `out`; columns >= floor(L/ratio) up to
- * gstride are set to -inf.  Rows whose L is outside [0, gstride*ratio]
- * get all -inf. */
+ * gstride are set to -inf.  Rows with L < 0 or floor(L/ratio) > gstride
+ * (more complete groups than the row holds) get all -inf. */
 void qo_scores(int n_rows, const int32_t* row_req, const int32_t* row_len, int Hi, int Di,
                int page, int ratio, const float* q_idx, const float* w_idx, const float* khat,
                const int32_t* page_table, int max_pages, int num_pages, int round_bf16,
@@ -105,7 +105,7 @@ void qo_scores(int n_rows, const int32_t* row_req, const int32_t* row_len, int H
 #pragma omp parallel for schedule(dynamic, 1)
   for (int r = 0; r < n_rows; ++r) {
     int L = row_len[r];
-    int G = (L >= 0 && L <= gstride * ratio) ? L / ratio : 0;
+    int G = (L >= 0 && L / ratio <= gstride) ? L / ratio : 0;
     const float* q = q_idx + (int64_t)r * Hi * Di;
     const float* w = w_idx + (int64_t)r * Hi;
     float* o = out + (int64_t)r * gstride;
