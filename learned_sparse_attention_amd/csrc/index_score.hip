@@ -1,0 +1,120 @@
+// index_score.hip — indexer scoring at decode: an fp32 GEMV per query row
+// over the request's paged compressed keys k̂.
+//
+// Per complete group g of the row (the C4 groups of the "QSA in brief"
+// section of the Qwen3.8-27B QSA model card; the scoring form is the
+// library's stated reading, since the pages give none):
+//   score[g] = sum_h w[h] * max(0, sum_d q[h,d] * khat[g,h,d])
+//
+// The work is a stream over k̂ (2 KiB per group, 0.5 flop per byte), so the
+// kernel is built for HBM bandwidth, not arithmetic:
+//   - one wavefront consumes one 32 KiB k̂ page (16 groups) with fully
+//     coalesced 16-byte loads: lane l reads float4 #l of each 1 KiB half of
+//     a group, i.e. heads l/16 and 4 + l/16, dims 4*(l%16) .. +3;
+//   - each lane keeps the matching 8 query values and 2 weights in
+//     registers for the whole launch;
+//   - per-head dot products finish with DPP row reductions (a DPP row is
+//     exactly the 16 lanes that hold one head);
+//   - the 16 group scores are transposed so lanes 0..15 own one group each,
+//     summed across the 4 rows with two cross-row shuffles and stored as
+//     one 64-byte coalesced write.
+#include "qsa_device.h"
+#include "qsa_launch.h"
+
+namespace qsa {
+namespace {
+
+constexpr int kScoreThreads = 256;  // 4 waves, one k̂ page each per step
+constexpr int kPagesPerBlock = 8;
+
+__device__ __forceinline__ float dot4(float4 a, float4 b) {
+  return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+}
+
+__device__ __forceinline__ float4 round4(float4 a) {
+  return make_float4(bf16_round(a.x), bf16_round(a.y), bf16_round(a.z), bf16_round(a.w));
+}
+
+template <bool kRound>
+__global__ __launch_bounds__(kScoreThreads) void index_score_gemv_kernel(
+    const float* __restrict__ khat, const int32_t* __restrict__ page_table, int max_pages,
+    int num_pages, const int32_t* __restrict__ row_req, const int32_t* __restrict__ row_len,
+    int req0, int first_pos, int max_ctx, const float* __restrict__ q_idx,
+    const float* __restrict__ w_idx, float* __restrict__ scores, int gstride) {
+  // rows carry their own (request, length); with row_req null, row r uses
+  // page-table row r; with both null, rows are the consecutive queries of
+  // request req0 starting at position first_pos
+  const int row = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int L = row_len ? row_len[row] : first_pos + row + 1;
+  const int G = (L >= 0 && L <= max_ctx) ? L / kRatio : 0;
+  const int req = row_req ? row_req[row] : (row_len ? row : req0);
+
+  const int hA = lane >> 4, hB = 4 + (lane >> 4), d0 = 4 * (lane & 15);
+  const float* qrow = q_idx + (size_t)row * kGroupFloats;
+  float4 qa = *reinterpret_cast<const float4*>(qrow + hA * kIdxDim + d0);
+  float4 qb = *reinterpret_cast<const float4*>(qrow + hB * kIdxDim + d0);
+  if (kRound) { qa = round4(qa); qb = round4(qb); }
+  const float wa = w_idx[(size_t)row * kIdxHeads + hA];
+  const float wb = w_idx[(size_t)row * kIdxHeads + hB];
+
+  float* srow = scores + (size_t)row * gstride;
+  const int row_pages = (gstride + kGroupsPerPage - 1) / kGroupsPerPage;
+  const int* pt = page_table + (size_t)req * max_pages;
+
+  for (int i = 0; i < kPagesPerBlock / 4; ++i) {
+    const int page = blockIdx.x * kPagesPerBlock + i * 4 + wave;
+    if (page >= row_pages) break;
+    const int g0 = page * kGroupsPerPage;
+    float sc = -INFINITY;
+    if (g0 < G) {
+      const int phys = pt[page];
+      if (phys >= 0 && phys < num_pages) {
+        const float4* base =
+            reinterpret_cast<const float4*>(khat + (size_t)phys * kGroupsPerPage * kGroupFloats);
+        float v[kGroupsPerPage];
+#pragma unroll
+        for (int g = 0; g < kGroupsPerPage; ++g) {
+          float4 x0 = base[g * 128 + lane];
+          float4 x1 = base[g * 128 + 64 + lane];
+          if (kRound) { x0 = round4(x0); x1 = round4(x1); }
+          float p0 = row16_sum(dot4(x0, qa));
+          float p1 = row16_sum(dot4(x1, qb));
+          v[g] = wa * fmaxf(p0, 0.0f) + wb * fmaxf(p1, 0.0f);
+        }
+        // lane l keeps its row's partial of group l % 16
+        float keep = v[0];
+#pragma unroll
+        for (int g = 1; g < kGroupsPerPage; ++g) keep = ((lane & 15) == g) ? v[g] : keep;
+        keep += __shfl_xor(keep, 16, kWave);
+        keep += __shfl_xor(keep, 32, kWave);
+        if (g0 + (lane & 15) < G) sc = keep + 0.0f;  // -0 -> +0
+      }
+    }
+    if (lane < kGroupsPerPage && g0 + lane < gstride) srow[g0 + lane] = sc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_index_score_gemv(const float* khat, const int32_t* page_table, int max_pages,
+                                   int num_pages, int n_rows, const int32_t* row_req,
+                                   const int32_t* row_len, int req0, int first_pos, int max_ctx,
+                                   const float* q_idx, const float* w_idx, float* scores,
+                                   int gstride, bool round_bf16, hipStream_t stream) {
+  if (n_rows <= 0 || gstride <= 0) return hipSuccess;
+  const int row_pages = (gstride + kGroupsPerPage - 1) / kGroupsPerPage;
+  dim3 grid((row_pages + kPagesPerBlock - 1) / kPagesPerBlock, n_rows, 1);
+  if (round_bf16)
+    hipLaunchKernelGGL(index_score_gemv_kernel<true>, grid, dim3(kScoreThreads), 0, stream, khat,
+                       page_table, max_pages, num_pages, row_req, row_len, req0, first_pos, max_ctx,
+                       q_idx, w_idx, scores, gstride);
+  else
+    hipLaunchKernelGGL(index_score_gemv_kernel<false>, grid, dim3(kScoreThreads), 0, stream, khat,
+                       page_table, max_pages, num_pages, row_req, row_len, req0, first_pos, max_ctx,
+                       q_idx, w_idx, scores, gstride);
+  return hipGetLastError();
+}
+
+}  // namespace qsa

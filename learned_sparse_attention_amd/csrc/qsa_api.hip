@@ -1,0 +1,278 @@
+// qsa_api.hip — the C ABI of libqsa (declared in include/qsa.h): argument
+// and geometry checks on the host, workspace carving, and the launch
+// sequence of each entry point on the caller's stream.  No call allocates,
+// synchronises or copies device data to the host.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qsa.h"
+#include "qsa_device.h"
+#include "qsa_launch.h"
+
+namespace {
+
+using namespace qsa;
+
+constexpr int kCapacity = 262144;  // tokens per request (qsa-hisparse offload contract)
+constexpr int kMaxRows = 64;       // query rows per KV head and request
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int gstride_of(int max_ctx) { return max_ctx / kRatio; }
+
+// Decode attention: selection entries per split-K workgroup.  Aims at
+// roughly 512 workgroups over the whole batch, with at least 16 groups (64
+// tokens, one 16-token sub-tile per wavefront) per workgroup.
+int groups_per_split(const qsa_geometry* g, int batch, int q_per_req) {
+  const int gq = g->num_q_heads / g->num_kv_heads;
+  const int nblk = (q_per_req * gq + 15) / 16;
+  const long long items = (long long)batch * g->num_kv_heads * nblk;
+  long long gps = ((long long)g->topk_groups * items + 511) / 512;
+  gps = (gps + 15) / 16 * 16;
+  if (gps < 16) gps = 16;
+  if (gps > g->topk_groups) gps = (g->topk_groups + 15) / 16 * 16;
+  return (int)gps;
+}
+
+struct DecodeLayout {
+  int gps, n_splits, gstride;
+  size_t off_scores, off_sel, off_partial, total;
+};
+
+DecodeLayout decode_layout(const qsa_geometry* g, int batch, int q_per_req, int max_ctx) {
+  DecodeLayout d;
+  d.gps = groups_per_split(g, batch, q_per_req);
+  d.n_splits = (g->topk_groups + d.gps - 1) / d.gps;
+  d.gstride = gstride_of(max_ctx);
+  const int rows = q_per_req * (g->num_q_heads / g->num_kv_heads);
+  size_t off = 0;
+  d.off_scores = off;
+  off += align_up(sizeof(float) * (size_t)batch * d.gstride);
+  d.off_sel = off;
+  off += align_up(sizeof(int32_t) * (size_t)batch * g->topk_groups);
+  d.off_partial = off;
+  off += align_up(sizeof(float) * (size_t)batch * g->num_kv_heads * d.n_splits * rows *
+                  (2 + kHeadDim));
+  d.total = off;
+  return d;
+}
+
+struct RowsLayout {
+  int gstride;
+  size_t off_scores, off_sel, total;
+};
+
+RowsLayout rows_layout(const qsa_geometry* g, int n_rows, int max_ctx) {
+  RowsLayout r;
+  r.gstride = gstride_of(max_ctx);
+  size_t off = 0;
+  r.off_scores = off;
+  off += align_up(sizeof(float) * (size_t)n_rows * r.gstride);
+  r.off_sel = off;
+  off += align_up(sizeof(int32_t) * (size_t)n_rows * g->topk_groups);
+  r.total = off;
+  return r;
+}
+
+bool cache_ok(const qsa_paged_cache* c, bool need_kv) {
+  if (!c || !c->khat || !c->page_table || c->max_pages <= 0 || c->num_pages <= 0) return false;
+  if (need_kv && (!c->k || !c->v)) return false;
+  return true;
+}
+
+qsa_status ws_ok(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return QSA_OK;
+  if (!ws || ws_bytes < need || ((uintptr_t)ws % kAlign) != 0) return QSA_ERR_WORKSPACE;
+  return QSA_OK;
+}
+
+float scale_of(const qsa_geometry* g) {
+  return g->sm_scale > 0.0f ? g->sm_scale : 1.0f / sqrtf((float)g->head_dim);
+}
+
+AttnArgs attn_args(const qsa_geometry* g, const qsa_paged_cache* c) {
+  AttnArgs a = {};
+  a.k = c->k;
+  a.v = c->v;
+  a.kv_dtype = g->kv_dtype;
+  a.page_table = c->page_table;
+  a.max_pages = c->max_pages;
+  a.num_pages = c->num_pages;
+  a.K = g->topk_groups;
+  a.Hq = g->num_q_heads;
+  a.Hkv = g->num_kv_heads;
+  a.sm_scale = scale_of(g);
+  a.k_scale = g->k_scale;
+  a.v_scale = g->v_scale;
+  return a;
+}
+
+#define QSA_HIP(call)                                \
+  do {                                               \
+    if ((call) != hipSuccess) return QSA_ERR_HIP;    \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* qsa_status_string(qsa_status s) {
+  switch (s) {
+    case QSA_OK: return "ok";
+    case QSA_ERR_INVALID_ARG: return "invalid argument";
+    case QSA_ERR_UNSUPPORTED: return "unsupported geometry";
+    case QSA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case QSA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+qsa_status qsa_validate(const qsa_geometry* g) {
+  if (!g) return QSA_ERR_INVALID_ARG;
+  if (g->head_dim != kHeadDim || g->page_size != kPage || g->compress_ratio != kRatio ||
+      g->idx_heads != kIdxHeads || g->idx_dim != kIdxDim)
+    return QSA_ERR_UNSUPPORTED;
+  if (g->topk_groups < 1 || g->topk_groups > 2048) return QSA_ERR_UNSUPPORTED;
+  if (g->num_kv_heads < 1 || g->num_q_heads < g->num_kv_heads ||
+      g->num_q_heads % g->num_kv_heads != 0 || g->num_q_heads / g->num_kv_heads > 16)
+    return QSA_ERR_UNSUPPORTED;
+  if (g->kv_dtype != QSA_KV_BF16 && g->kv_dtype != QSA_KV_FP8_E4M3) return QSA_ERR_UNSUPPORTED;
+  if (!(g->k_scale > 0.0f) || !(g->v_scale > 0.0f) || !isfinite(g->k_scale) ||
+      !isfinite(g->v_scale) || !isfinite(g->sm_scale))
+    return QSA_ERR_INVALID_ARG;
+  return QSA_OK;
+}
+
+int32_t qsa_token_width(const qsa_geometry* g, int32_t q_per_req) {
+  if (qsa_validate(g) != QSA_OK || q_per_req < 1 || q_per_req > 4) return 0;
+  return kRatio * g->topk_groups + (kRatio - 1) + (q_per_req - 1);
+}
+
+size_t qsa_index_topk_workspace_size(const qsa_geometry* g, int32_t n_rows, int32_t max_ctx) {
+  if (qsa_validate(g) != QSA_OK || n_rows < 0 || max_ctx < 1 || max_ctx > kCapacity) return 0;
+  return rows_layout(g, n_rows, max_ctx).total;
+}
+
+size_t qsa_decode_workspace_size(const qsa_geometry* g, int32_t batch, int32_t q_per_req,
+                                 int32_t max_ctx) {
+  if (qsa_validate(g) != QSA_OK || batch < 0 || q_per_req < 1 || q_per_req > 4 || max_ctx < 1 ||
+      max_ctx > kCapacity || q_per_req * (g->num_q_heads / g->num_kv_heads) > kMaxRows)
+    return 0;
+  return decode_layout(g, batch, q_per_req, max_ctx).total;
+}
+
+size_t qsa_prefill_workspace_size(const qsa_geometry* g, int32_t n_q, int32_t max_ctx) {
+  if (qsa_validate(g) != QSA_OK || n_q < 0 || max_ctx < 1 || max_ctx > kCapacity) return 0;
+  return rows_layout(g, n_q, max_ctx).total;
+}
+
+qsa_status qsa_index_topk(const qsa_geometry* g, const qsa_paged_cache* cache, int32_t n_rows,
+                          int32_t max_ctx, const int32_t* row_req, const int32_t* row_len,
+                          const float* q_idx, const float* w_idx, int32_t* out_groups,
+                          float* out_scores, void* ws, size_t ws_bytes, void* stream) {
+  qsa_status st = qsa_validate(g);
+  if (st != QSA_OK) return st;
+  if (n_rows < 0 || max_ctx < 1 || max_ctx > kCapacity || !cache_ok(cache, false))
+    return QSA_ERR_INVALID_ARG;
+  if (max_ctx > cache->max_pages * kPage) return QSA_ERR_INVALID_ARG;
+  if (n_rows == 0) return QSA_OK;
+  if (!row_req || !row_len || !q_idx || !w_idx || !out_groups) return QSA_ERR_INVALID_ARG;
+  const RowsLayout lay = rows_layout(g, n_rows, max_ctx);
+  if (!out_scores && (st = ws_ok(ws, ws_bytes, lay.off_sel)) != QSA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  float* scores = out_scores ? out_scores : (float*)((char*)ws + lay.off_scores);
+  QSA_HIP(launch_index_score_gemv(cache->khat, cache->page_table, cache->max_pages,
+                                  cache->num_pages, n_rows, row_req, row_len, 0, 0, max_ctx,
+                                  q_idx, w_idx, scores, lay.gstride, false, s));
+  QSA_HIP(launch_topk(scores, lay.gstride, n_rows, row_len, 0, max_ctx, g->topk_groups,
+                      out_groups, s));
+  return QSA_OK;
+}
+
+qsa_status qsa_decode(const qsa_geometry* g, const qsa_paged_cache* cache, int32_t batch,
+                      int32_t q_per_req, int32_t max_ctx, const int32_t* ctx_lens,
+                      const float* q_idx, const float* w_idx, const uint16_t* q, float* out,
+                      int32_t* out_groups, int32_t* out_tokens, float* out_scores, void* ws,
+                      size_t ws_bytes, void* stream) {
+  qsa_status st = qsa_validate(g);
+  if (st != QSA_OK) return st;
+  if (batch < 0 || q_per_req < 1 || q_per_req > 4 || max_ctx < 1 || max_ctx > kCapacity ||
+      !cache_ok(cache, true))
+    return QSA_ERR_INVALID_ARG;
+  if (q_per_req * (g->num_q_heads / g->num_kv_heads) > kMaxRows) return QSA_ERR_UNSUPPORTED;
+  if (max_ctx > cache->max_pages * kPage) return QSA_ERR_INVALID_ARG;
+  if (batch == 0) return QSA_OK;
+  if (!ctx_lens || !q_idx || !w_idx || !q || !out) return QSA_ERR_INVALID_ARG;
+  const DecodeLayout lay = decode_layout(g, batch, q_per_req, max_ctx);
+  if ((st = ws_ok(ws, ws_bytes, lay.total)) != QSA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  float* scores = out_scores ? out_scores : (float*)(w + lay.off_scores);
+  int32_t* sel = out_groups ? out_groups : (int32_t*)(w + lay.off_sel);
+  // the indexer runs on the base position; draft positions reuse its selection
+  QSA_HIP(launch_index_score_gemv(cache->khat, cache->page_table, cache->max_pages,
+                                  cache->num_pages, batch, nullptr, ctx_lens, 0, 0,
+                                  max_ctx - (q_per_req - 1), q_idx, w_idx, scores, lay.gstride,
+                                  false, s));
+  QSA_HIP(launch_topk(scores, lay.gstride, batch, ctx_lens, 0, max_ctx - (q_per_req - 1),
+                      g->topk_groups, sel, s));
+  AttnArgs a = attn_args(g, cache);
+  a.sel = sel;
+  a.ctx_lens = ctx_lens;
+  a.max_ctx = max_ctx;
+  a.q_per_req = q_per_req;
+  a.q = q;
+  a.batch = batch;
+  a.groups_per_split = lay.gps;
+  a.n_splits = lay.n_splits;
+  a.partial = (float*)(w + lay.off_partial);
+  a.out = out;
+  QSA_HIP(launch_sparse_attn_decode(a, s));
+  if (out_tokens)
+    QSA_HIP(launch_expand_tokens(sel, g->topk_groups, batch, q_per_req, ctx_lens, 0, max_ctx,
+                                 qsa_token_width(g, q_per_req), out_tokens, s));
+  return QSA_OK;
+}
+
+qsa_status qsa_prefill(const qsa_geometry* g, const qsa_paged_cache* cache, int32_t req,
+                       int32_t first_pos, int32_t n_q, const float* q_idx, const float* w_idx,
+                       const uint16_t* q, float* out, int32_t* out_groups, int32_t* out_tokens,
+                       float* out_scores, void* ws, size_t ws_bytes, void* stream) {
+  qsa_status st = qsa_validate(g);
+  if (st != QSA_OK) return st;
+  if (req < 0 || first_pos < 0 || n_q < 0 || !cache_ok(cache, true)) return QSA_ERR_INVALID_ARG;
+  const long long total = (long long)first_pos + n_q;
+  if (total > kCapacity || total > (long long)cache->max_pages * kPage) return QSA_ERR_INVALID_ARG;
+  if (n_q == 0) return QSA_OK;
+  if (!q_idx || !w_idx || !q || !out) return QSA_ERR_INVALID_ARG;
+  const int max_ctx = (int)total;
+  const RowsLayout lay = rows_layout(g, n_q, max_ctx);
+  if ((st = ws_ok(ws, ws_bytes, lay.total)) != QSA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  float* scores = out_scores ? out_scores : (float*)(w + lay.off_scores);
+  int32_t* sel = out_groups ? out_groups : (int32_t*)(w + lay.off_sel);
+  QSA_HIP(launch_index_score_gemv(cache->khat, cache->page_table, cache->max_pages,
+                                  cache->num_pages, n_q, nullptr, nullptr, req, first_pos,
+                                  max_ctx, q_idx, w_idx, scores, lay.gstride, true, s));
+  QSA_HIP(launch_topk(scores, lay.gstride, n_q, nullptr, first_pos, max_ctx, g->topk_groups, sel,
+                      s));
+  AttnArgs a = attn_args(g, cache);
+  a.sel = sel;
+  a.first_pos = first_pos;
+  a.req = req;
+  a.max_ctx = max_ctx;
+  a.q_per_req = 1;
+  a.q = q;
+  a.batch = n_q;
+  a.out = out;
+  QSA_HIP(launch_sparse_attn_prefill(a, s));
+  if (out_tokens)
+    QSA_HIP(launch_expand_tokens(sel, g->topk_groups, n_q, 1, nullptr, first_pos, max_ctx,
+                                 qsa_token_width(g, 1), out_tokens, s));
+  return QSA_OK;
+}
+
+}  // extern "C"

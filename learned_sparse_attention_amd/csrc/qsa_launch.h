@@ -1,0 +1,67 @@
+// qsa_launch.h — internal host-side launchers of the QSA kernels.
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+// Indexer scores of `n_rows` query rows over their request's paged k̂
+// (fp32 GEMV).  scores is [n_rows, gstride]; columns g >= floor(L/4) get
+// -inf.  Rows take (request, L) from row_req/row_len; with row_req null,
+// row r uses page-table row r; with both null, rows are queries
+// first_pos + row of request req0.  round_bf16 rounds
+// q_idx and k̂ to bf16 before the products.
+hipError_t launch_index_score_gemv(const float* khat, const int32_t* page_table, int max_pages,
+                                   int num_pages, int n_rows, const int32_t* row_req,
+                                   const int32_t* row_len, int req0, int first_pos, int max_ctx,
+                                   const float* q_idx, const float* w_idx, float* scores,
+                                   int gstride, bool round_bf16, hipStream_t stream);
+
+// Indexer scores of a prefill chunk on the matrix cores (bf16 operands,
+// fp32 accumulation): query i of the chunk has L = first_pos + i + 1.
+hipError_t launch_index_score_prefill(const float* khat, const int32_t* page_table,
+                                      int max_pages, int num_pages, int req, int first_pos,
+                                      int n_q, const float* q_idx, const float* w_idx,
+                                      float* scores, int gstride, hipStream_t stream);
+
+// Exact top-K of each row: candidates g < G(row) where G = floor(L/4) for
+// L = row_len[row] in [0, max_ctx] (else G = 0); when row_len is null,
+// L = first_pos + row + 1.  out is [n_rows, K] ascending, -1 padded.
+hipError_t launch_topk(const float* scores, int gstride, int n_rows, const int32_t* row_len,
+                       int first_pos, int max_ctx, int K, int32_t* out, hipStream_t stream);
+
+struct AttnArgs {
+  const void* k;
+  const void* v;
+  int kv_dtype;  // 0 bf16, 1 fp8 e4m3
+  const int32_t* page_table;
+  int max_pages;
+  int num_pages;
+  const int32_t* sel;  // [items, K] ascending group ids, -1 padded
+  int K;
+  const int32_t* ctx_lens;  // decode: [B] L0; prefill: null
+  int first_pos;            // prefill: position of query 0
+  int req;                  // prefill: page-table row
+  int max_ctx;
+  int q_per_req;
+  const uint16_t* q;  // decode [B, Q, Hq, D]; prefill [n_q, Hq, D]
+  int Hq, Hkv;
+  float sm_scale, k_scale, v_scale;
+  int batch;            // decode: requests; prefill: queries
+  int groups_per_split; // decode split size (groups)
+  int n_splits;
+  float* partial;  // decode: [B, Hkv, n_splits, Q*Hq/Hkv, 2 + D]
+  float* out;      // prefill: [n_q, Hq, D]; decode: [B, Q, Hq, D] (combine)
+};
+
+hipError_t launch_sparse_attn_decode(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_sparse_attn_prefill(const AttnArgs& a, hipStream_t stream);
+
+// Expanded token lists: [rows, q_per_req, width], ascending, -1 padded.
+hipError_t launch_expand_tokens(const int32_t* sel, int K, int n_rows, int q_per_req,
+                                const int32_t* ctx_lens, int first_pos, int max_ctx, int width,
+                                int32_t* out, hipStream_t stream);
+
+}  // namespace qsa

@@ -1,0 +1,485 @@
+// sparse_attn.hip — grouped-query attention over the expanded QSA token
+// selection, read straight from the paged KV cache.
+//
+// Each selected group g stands for tokens 4g..4g+3 (selections address
+// single tokens: TensorRT-LLM QSASparseAttentionConfig,
+// get_indices_block_size); the current partial block and, for draft
+// positions, the groups completed since the base position follow as one
+// contiguous token range (index_share_for_mtp_iteration).  Query head h
+// reads KV head h / (Hq / Hkv); a row with no visible token yields zeros
+// (OrcaRouter article on SGLang PR #41855, zero-output convention).
+//
+// One workgroup (4 wavefronts) owns one work item: a KV head, a slice of the
+// selection list and the query rows that share it (the GQA heads of one
+// query, or of every draft position of a request).  The item's token
+// stream is translated once into physical row offsets in LDS; then each
+// wavefront walks 16-token sub-tiles of it:
+//   S^T[16 tok x 16 rows] = K[16 tok x 256] . Q^T     (8 x mfma 16x16x32 bf16)
+//   online softmax per query row (exp2 domain, fp32)
+//   O^T[256 x 16 rows]   += V^T[256 x 16 tok] . P^T   (2 x 16 x mfma 16x16x16 bf16,
+//                                                      P as a bf16 hi + lo pair)
+// K and V go from HBM to registers already in MFMA operand order: lane l
+// reads 64 contiguous bytes of token l%16's K row and 16 contiguous bytes
+// of four V rows, so no LDS staging or transposition is needed; FP8 E4M3
+// elements are widened to bf16 exactly by the hardware converter and the
+// per-tensor scales are folded into the logit scale and the final output.
+// The contraction dimension is permuted consistently between the two MFMA
+// operands (dot products do not depend on the order of d), which is what
+// makes those contiguous loads possible.  Waves merge their (max, sum,
+// accumulator) through LDS at the end.  Decode splits the selection over
+// several workgroups and writes (max, sum, accumulator) partials that
+// combine_kernel merges; prefill writes normalised rows directly.
+#include "qsa_device.h"
+#include "qsa_launch.h"
+
+namespace qsa {
+namespace {
+
+constexpr int kAttnThreads = 256;
+constexpr int kAttnWaves = kAttnThreads / kWave;
+constexpr int kAccPitch = kHeadDim + 1;  // LDS row pitch of the merged accumulator
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+struct ItemDesc {
+  int req;           // page-table row
+  const int32_t* sel;
+  int g_begin, g_end;  // selection-list entries of this item
+  int x_begin, x_end;  // contiguous extra tokens of this item
+  int base_len;        // query row r sees extra tokens t < base_len + r / gq
+};
+
+// Widen 8 FP8 bytes (two dwords) to 8 bf16 (an MFMA operand).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  u32x4 r;
+  r.x = fp8x2_to_bf16x2<false>(lo);
+  r.y = fp8x2_to_bf16x2<true>(lo);
+  r.z = fp8x2_to_bf16x2<false>(hi);
+  r.w = fp8x2_to_bf16x2<true>(hi);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Rows handled: global query rows row_base .. row_base + 16*NB - 1 of the
+// item (row r = position r / gq, head r % gq of the KV head's group), of
+// which those < n_rows exist.
+template <bool kFp8, int NB>
+__device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& it, int kvh,
+                                            const uint16_t* q_rows, int q_row_stride,
+                                            int row_base, int n_rows, int gq, float* acc_lds,
+                                            float* ml_lds, int32_t* tok_row, float* out_final,
+                                            float* out_partial) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int lq = lane & 15, lg = lane >> 4;
+  constexpr int kEsize = kFp8 ? 1 : 2;
+  constexpr int kRowBytes = kHeadDim * kEsize;
+
+  // ---- token stream -> physical row offsets (page * 64 + slot), -1 if absent
+  const int n_groups = max(0, it.g_end - it.g_begin);
+  const int n_extra = max(0, it.x_end - it.x_begin);
+  const int n_stream = 4 * n_groups + n_extra;
+  const int n_sub = (n_stream + 15) / 16;
+  const int32_t* pt = a.page_table + (size_t)it.req * a.max_pages;
+  for (int i = tid; i < n_sub * 16; i += kAttnThreads) {
+    int t = -1;
+    if (i < 4 * n_groups) {
+      const int g = it.sel[it.g_begin + i / 4];
+      t = g >= 0 ? 4 * g + (i & 3) : -1;
+    } else if (i < n_stream) {
+      t = it.x_begin + (i - 4 * n_groups);
+    }
+    int r = -1;
+    if (t >= 0) {
+      const int phys = pt[t / kPage];
+      if (phys >= 0 && phys < a.num_pages) r = phys * kPage + (t % kPage);
+    }
+    tok_row[i] = r;
+  }
+  __syncthreads();
+
+  // ---- query operands: lane supplies Q[row 16*nb + lq][64*lg + 8*ks + 0..7]
+  bf16x8 qop[NB][8];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int r = row_base + nb * 16 + lq;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (r < n_rows) {
+        const uint16_t* qp = q_rows + (size_t)(r / gq) * q_row_stride + (size_t)(r % gq) * kHeadDim;
+        v = *reinterpret_cast<const u32x4*>(qp + 64 * lg + 8 * ks);
+      }
+      qop[nb][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  // causal limit of this lane's query rows (only extra tokens can exceed it)
+  int limit[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) limit[nb] = it.base_len + (row_base + nb * 16 + lq) / gq;
+
+  const float qk_scale = a.sm_scale * a.k_scale * kLog2e;
+  float m_run[NB], l_run[NB];
+  float4_t acc[NB][16];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    m_run[nb] = -INFINITY;
+    l_run[nb] = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < 16; ++mb) acc[nb][mb] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  }
+
+  const uint8_t* kc = reinterpret_cast<const uint8_t*>(a.k);
+  const uint8_t* vc = reinterpret_cast<const uint8_t*>(a.v);
+  const int Hkv = a.Hkv;
+
+  for (int s = wave; s < n_sub; s += kAttnWaves) {
+    // K: token 16s + lq, bytes [64*lg*esize, +64*esize) of its row
+    const int rk = tok_row[16 * s + lq];
+    const uint8_t* kp = kc + ((size_t)max(rk, 0) * Hkv + kvh) * kRowBytes + 64 * lg * kEsize;
+    u32x4 kraw[kFp8 ? 4 : 8];
+#pragma unroll
+    for (int i = 0; i < (kFp8 ? 4 : 8); ++i) kraw[i] = reinterpret_cast<const u32x4*>(kp)[i];
+    // V: tokens 16s + 4*lg + j, bytes [16*lq*esize, +16*esize)
+    int rv[4];
+    u32x4 vraw[4][kFp8 ? 1 : 2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      rv[j] = tok_row[16 * s + 4 * lg + j];
+      const uint8_t* vp = vc + ((size_t)max(rv[j], 0) * Hkv + kvh) * kRowBytes + 16 * lq * kEsize;
+#pragma unroll
+      for (int i = 0; i < (kFp8 ? 1 : 2); ++i) vraw[j][i] = reinterpret_cast<const u32x4*>(vp)[i];
+    }
+
+    // S^T = K . Q^T
+    float4_t sc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) sc[nb] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      bf16x8 kop;
+      if (kFp8) {
+        const u32x4 w = kraw[ks / 2];
+        kop = (ks & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
+      } else {
+        kop = __builtin_bit_cast(bf16x8, kraw[ks]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[nb][ks], sc[nb], 0, 0, 0);
+    }
+
+    // token of D row 4*lg + i is stream entry 16s + 4*lg + i (= V token i)
+    bool tok_ok[4];
+    int tok_id[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int si = 16 * s + 4 * lg + i;
+      tok_ok[i] = rv[i] >= 0;
+      tok_id[i] = si < 4 * n_groups ? -1 : it.x_begin + (si - 4 * n_groups);  // -1: always visible
+    }
+
+    // online softmax, one query row per lane (replicated over the 4 lane
+    // groups).  The weights enter the PV product as a bf16 pair hi + lo
+    // (hi = bf16(p), lo = bf16(p - hi)), i.e. with ~16 significant bits, so
+    // the bf16 operand rounding does not show in outputs of few tokens.
+    short4_t pb_hi[NB], pb_lo[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float sv[4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool vis = tok_ok[i] && (tok_id[i] < limit[nb]);
+        sv[i] = vis ? sc[nb][i] * qk_scale : -INFINITY;
+        tmax = fmaxf(tmax, sv[i]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      const float m_new = fmaxf(m_run[nb], tmax);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run[nb] - m_new);
+      float psum = 0.0f;
+      uint32_t hb[4], lb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = (m_new == -INFINITY) ? 0.0f : exp2f(sv[i] - m_new);
+        hb[i] = bf16_rne_bits(p);
+        lb[i] = bf16_rne_bits(p - __uint_as_float(hb[i] << 16));
+        psum += p;
+      }
+      l_run[nb] = l_run[nb] * alpha + psum;
+      m_run[nb] = m_new;
+#pragma unroll
+      for (int mb = 0; mb < 16; ++mb) acc[nb][mb] *= alpha;
+      pb_hi[nb] = (short4_t){(short)hb[0], (short)hb[1], (short)hb[2], (short)hb[3]};
+      pb_lo[nb] = (short4_t){(short)lb[0], (short)lb[1], (short)lb[2], (short)lb[3]};
+    }
+
+    // O^T += V^T . P^T; m-block mb holds d = 64*lg' + 16*i + mb for D row 4*lg' + i
+    uint32_t cv[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (kFp8) {
+        const u32x4 w = tok_ok[j] ? vraw[j][0] : (u32x4){0u, 0u, 0u, 0u};
+        cv[j][0] = fp8x2_to_bf16x2<false>(w.x); cv[j][1] = fp8x2_to_bf16x2<true>(w.x);
+        cv[j][2] = fp8x2_to_bf16x2<false>(w.y); cv[j][3] = fp8x2_to_bf16x2<true>(w.y);
+        cv[j][4] = fp8x2_to_bf16x2<false>(w.z); cv[j][5] = fp8x2_to_bf16x2<true>(w.z);
+        cv[j][6] = fp8x2_to_bf16x2<false>(w.w); cv[j][7] = fp8x2_to_bf16x2<true>(w.w);
+      } else {
+        const u32x4 w0 = tok_ok[j] ? vraw[j][0] : (u32x4){0u, 0u, 0u, 0u};
+        const u32x4 w1 = tok_ok[j] ? vraw[j][1] : (u32x4){0u, 0u, 0u, 0u};
+        cv[j][0] = w0.x; cv[j][1] = w0.y; cv[j][2] = w0.z; cv[j][3] = w0.w;
+        cv[j][4] = w1.x; cv[j][5] = w1.y; cv[j][6] = w1.z; cv[j][7] = w1.w;
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 16; ++mb) {
+      const int qd = mb >> 1;
+      const uint32_t sel = (mb & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t lo = __builtin_amdgcn_perm(cv[1][qd], cv[0][qd], sel);
+      const uint32_t hi = __builtin_amdgcn_perm(cv[3][qd], cv[2][qd], sel);
+      const short4_t vop = __builtin_bit_cast(short4_t, (u32x2){lo, hi});
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pb_hi[nb], acc[nb][mb], 0, 0, 0);
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pb_lo[nb], acc[nb][mb], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- merge the 4 waves: row maxima and sums, then accumulators in order
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float l = l_run[nb];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    if (lg == 0) {
+      ml_lds[(wave * NB + nb) * 32 + lq] = m_run[nb];
+      ml_lds[(wave * NB + nb) * 32 + 16 + lq] = l;
+    }
+  }
+  __syncthreads();
+  float fac[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float M = -INFINITY;
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, ml_lds[(w * NB + nb) * 32 + lq]);
+    fac[nb] = (M == -INFINITY) ? 0.0f : exp2f(m_run[nb] - M);
+  }
+  for (int w = 0; w < kAttnWaves; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        float* rowp = acc_lds + (size_t)(nb * 16 + lq) * kAccPitch;
+#pragma unroll
+        for (int mb = 0; mb < 16; ++mb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d = 64 * lg + 16 * i + mb;
+            const float v = acc[nb][mb][i] * fac[nb];
+            rowp[d] = (w == 0) ? v : rowp[d] + v;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- write: normalised rows, or (max, sum, accumulator) partials
+  for (int r = 0; r < min(16 * NB, n_rows - row_base); ++r) {
+    const int nb = r / 16, rl = r % 16;
+    float M = -INFINITY, Lsum = 0.0f;
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, ml_lds[(w * NB + nb) * 32 + rl]);
+    if (M != -INFINITY)
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float mw = ml_lds[(w * NB + nb) * 32 + rl];
+        if (mw != -INFINITY) Lsum += exp2f(mw - M) * ml_lds[(w * NB + nb) * 32 + 16 + rl];
+      }
+    const float* rowp = acc_lds + (size_t)r * kAccPitch;
+    for (int d = tid; d < kHeadDim; d += kAttnThreads) {
+      const int rg = row_base + r;
+      if (out_final) {
+        const float o = (Lsum > 0.0f) ? rowp[d] * (a.v_scale / Lsum) : 0.0f;
+        out_final[(size_t)(rg / gq) * ((size_t)a.Hq * kHeadDim) + (size_t)(rg % gq) * kHeadDim + d] = o;
+      } else {
+        float* pp = out_partial + (size_t)rg * (2 + kHeadDim);
+        if (d == 0) { pp[0] = M; pp[1] = Lsum; }
+        pp[2 + d] = rowp[d];
+      }
+    }
+  }
+}
+
+template <bool kFp8, int NB>
+__global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnArgs a) {
+  extern __shared__ float smem[];
+  const int gq = a.Hq / a.Hkv;
+  const int Q = a.q_per_req;
+  const int n_rows = Q * gq;
+  const int nblk = (n_rows + 16 * NB - 1) / (16 * NB);
+  const int split = blockIdx.x / nblk, rb = blockIdx.x % nblk;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  float* acc_lds = smem;
+  float* ml_lds = acc_lds + NB * 16 * kAccPitch;
+  int32_t* tok_row = reinterpret_cast<int32_t*>(ml_lds + kAttnWaves * NB * 32);
+
+  const int L0 = a.ctx_lens[b];
+  const bool valid = L0 >= 0 && L0 <= a.max_ctx - (Q - 1);
+  const int G = valid ? L0 / kRatio : 0;
+  const int n_valid = min(a.K, G);
+  ItemDesc it;
+  it.req = b;
+  it.sel = a.sel + (size_t)b * a.K;
+  it.g_begin = split * a.groups_per_split;
+  it.g_end = min(n_valid, it.g_begin + a.groups_per_split);
+  const bool last = split == a.n_splits - 1;
+  it.x_begin = kRatio * G;
+  it.x_end = (valid && last) ? L0 + Q - 1 : kRatio * G;
+  it.base_len = L0;
+
+  const uint16_t* q_rows = a.q + ((size_t)b * Q * a.Hq + (size_t)kvh * gq) * kHeadDim;
+  float* part = a.partial + (((size_t)b * a.Hkv + kvh) * a.n_splits + split) * n_rows * (2 + kHeadDim);
+  attend_item<kFp8, NB>(a, it, kvh, q_rows, a.Hq * kHeadDim, rb * 16 * NB, n_rows, gq, acc_lds,
+                        ml_lds, tok_row, nullptr, part);
+}
+
+template <bool kFp8, int NB>
+__global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(AttnArgs a) {
+  extern __shared__ float smem[];
+  const int qi = blockIdx.x, kvh = blockIdx.y;
+  const int gq = a.Hq / a.Hkv;
+  float* acc_lds = smem;
+  float* ml_lds = acc_lds + NB * 16 * kAccPitch;
+  int32_t* tok_row = reinterpret_cast<int32_t*>(ml_lds + kAttnWaves * NB * 32);
+
+  const int L = a.first_pos + qi + 1;
+  const int G = L / kRatio;
+  ItemDesc it;
+  it.req = a.req;
+  it.sel = a.sel + (size_t)qi * a.K;
+  it.g_begin = 0;
+  it.g_end = min(a.K, G);
+  it.x_begin = kRatio * G;
+  it.x_end = L;
+  it.base_len = L;
+  const uint16_t* q_rows = a.q + ((size_t)qi * a.Hq + (size_t)kvh * gq) * kHeadDim;
+  float* outp = a.out + ((size_t)qi * a.Hq + (size_t)kvh * gq) * kHeadDim;
+  attend_item<kFp8, NB>(a, it, kvh, q_rows, 0, 0, gq, gq, acc_lds, ml_lds, tok_row, outp, nullptr);
+}
+
+// Merge split partials: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+__global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restrict__ partial,
+                                                           int n_splits, int Hq, int Hkv, int Q,
+                                                           float v_scale, float* __restrict__ out) {
+  const int h = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int gq = Hq / Hkv, kvh = h / gq, r = j * gq + (h % gq);
+  const int R = Q * gq;
+  const float* p = partial + ((size_t)(b * Hkv + kvh) * n_splits) * R * (2 + kHeadDim) +
+                   (size_t)r * (2 + kHeadDim);
+  const size_t split_stride = (size_t)R * (2 + kHeadDim);
+  float M = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, p[s * split_stride]);
+  float num = 0.0f, den = 0.0f;
+  const int d = threadIdx.x;
+  if (M != -INFINITY) {
+    for (int s = 0; s < n_splits; ++s) {
+      const float* ps = p + s * split_stride;
+      const float m = ps[0];
+      if (m == -INFINITY) continue;
+      const float f = exp2f(m - M);
+      den += f * ps[1];
+      num += f * ps[2 + d];
+    }
+  }
+  out[(((size_t)b * Q + j) * Hq + h) * kHeadDim + d] = den > 0.0f ? num * (v_scale / den) : 0.0f;
+}
+
+// Token lists: slot i < 4*n_valid -> 4*sel[i/4] + i%4; then the extra range.
+__global__ void expand_tokens_kernel(const int32_t* __restrict__ sel, int K,
+                                     const int32_t* __restrict__ ctx_lens, int first_pos,
+                                     int max_ctx, int Q, int width, int32_t* __restrict__ out) {
+  const int row = blockIdx.x, j = blockIdx.y;
+  const int L0 = ctx_lens ? ctx_lens[row] : first_pos + row + 1;
+  const bool valid = L0 >= 0 && L0 <= max_ctx - (Q - 1);
+  const int G = valid ? L0 / kRatio : 0;
+  const int n_valid = min(K, G);
+  const int n_extra = valid ? L0 + j - kRatio * G : 0;
+  int32_t* o = out + ((size_t)row * Q + j) * width;
+  const int32_t* s = sel + (size_t)row * K;
+  for (int i = threadIdx.x; i < width; i += blockDim.x) {
+    int t = -1;
+    if (i < kRatio * n_valid) t = kRatio * s[i / kRatio] + (i % kRatio);
+    else if (i - kRatio * n_valid < n_extra) t = kRatio * G + (i - kRatio * n_valid);
+    o[i] = t;
+  }
+}
+
+size_t attn_smem_bytes(int NB, int stream_cap) {
+  return sizeof(float) * ((size_t)NB * 16 * kAccPitch + (size_t)kAttnWaves * NB * 32) +
+         sizeof(int32_t) * (size_t)((stream_cap + 15) / 16 * 16);
+}
+
+template <bool kFp8, int NB>
+hipError_t launch_decode_nb(const AttnArgs& a, hipStream_t stream) {
+  const int cap = 4 * a.groups_per_split + 3 + (a.q_per_req - 1);
+  const size_t smem = attn_smem_bytes(NB, cap);
+  const int rows = a.q_per_req * (a.Hq / a.Hkv);
+  const int nblk = (rows + 16 * NB - 1) / (16 * NB);
+  dim3 grid(a.n_splits * nblk, a.Hkv, a.batch);
+  hipLaunchKernelGGL((attn_decode_kernel<kFp8, NB>), grid, dim3(kAttnThreads), smem, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 cgrid(a.Hq, a.q_per_req, a.batch);
+  hipLaunchKernelGGL(combine_kernel, cgrid, dim3(kHeadDim), 0, stream, a.partial, a.n_splits, a.Hq,
+                     a.Hkv, a.q_per_req, a.v_scale, a.out);
+  return hipGetLastError();
+}
+
+template <bool kFp8, int NB>
+hipError_t launch_prefill_nb(const AttnArgs& a, hipStream_t stream) {
+  const int cap = 4 * a.K + 3;
+  const size_t smem = attn_smem_bytes(NB, cap);
+  dim3 grid(a.batch, a.Hkv);
+  hipLaunchKernelGGL((attn_prefill_kernel<kFp8, NB>), grid, dim3(kAttnThreads), smem, stream, a);
+  return hipGetLastError();
+}
+
+template <int NB>
+hipError_t dispatch_dtype(const AttnArgs& a, hipStream_t stream, bool prefill) {
+  if (a.kv_dtype == 1)
+    return prefill ? launch_prefill_nb<true, NB>(a, stream) : launch_decode_nb<true, NB>(a, stream);
+  return prefill ? launch_prefill_nb<false, NB>(a, stream) : launch_decode_nb<false, NB>(a, stream);
+}
+
+// One 16-row block per workgroup: query rows beyond 16 (e.g. 12 heads x 3
+// draft positions) take further workgroups over the same tokens, which
+// then mostly come from the caches.
+hipError_t dispatch(const AttnArgs& a, hipStream_t stream, bool prefill) {
+  if (prefill && a.Hq / a.Hkv > 16) return hipErrorInvalidValue;
+  return dispatch_dtype<1>(a, stream, prefill);
+}
+
+}  // namespace
+
+hipError_t launch_sparse_attn_decode(const AttnArgs& a, hipStream_t stream) {
+  if (a.batch <= 0) return hipSuccess;
+  return dispatch(a, stream, false);
+}
+
+hipError_t launch_sparse_attn_prefill(const AttnArgs& a, hipStream_t stream) {
+  if (a.batch <= 0) return hipSuccess;
+  return dispatch(a, stream, true);
+}
+
+hipError_t launch_expand_tokens(const int32_t* sel, int K, int n_rows, int q_per_req,
+                                const int32_t* ctx_lens, int first_pos, int max_ctx, int width,
+                                int32_t* out, hipStream_t stream) {
+  if (n_rows <= 0) return hipSuccess;
+  dim3 grid(n_rows, q_per_req);
+  hipLaunchKernelGGL(expand_tokens_kernel, grid, dim3(256), 0, stream, sel, K, ctx_lens, first_pos,
+                     max_ctx, q_per_req, width, out);
+  return hipGetLastError();
+}
+
+}  // namespace qsa

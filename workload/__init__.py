@@ -230,7 +230,7 @@ def decode_workload(seed: int, ctx_lens, q_per_req=1, num_q_heads=16, num_kv_hea
     stored = ctx + (q_per_req - 1)
     geom = geometry(num_q_heads, num_kv_heads, topk_groups, kv_dtype, sm_scale)
     mc = int(max_ctx) if max_ctx is not None else int(stored.max())
-    mc = ((mc + RATIO - 1) // RATIO) * RATIO
+    mc = max(RATIO, ((mc + RATIO - 1) // RATIO) * RATIO)
     pt, P = _paged_pool(seed, stored, random_pages, max_pages=(mc + PAGE - 1) // PAGE)
     geom, kc, vc, khat = _caches(seed, geom, stored, pt, P, idx_bf16_exact=False)
     q_idx = normal_f32(seed, T_QIDX, (B, HI, DI))
