@@ -1,0 +1,212 @@
+"""Benchmark of the QSA layer step on one MI355X.
+
+A step is one ``qsa_decode`` call (indexer scoring -> exact top-K ->
+expansion -> paged sparse GQA attention) on the headline workload: decode
+of 8 requests at 262,144 tokens each (65,536 C4 groups), FP8 E4M3 paged KV
+(page 64, random page table), Hq 16 / Hkv 2, head dim 256, K = 2,048 groups.
+Inputs are seeded and synthetic and resident in HBM before timing.
+
+Prints one JSON line: layer-steps/s, the roofline position of the dominant
+kernel (the indexer GEMV, HBM-bound) measured with HIP events on the stream
+it runs on, and the CPU oracle timed on this host as a reported baseline.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense BF16 MFMA (no sparsity)
+
+CONFIG_NAMES = {
+    1: "decode B1, L=8,193, BF16 KV, identity pages, K=512 groups",
+    2: "decode B8, L~U[32K,64K], FP8 KV, random pages, K=512 groups",
+    3: "decode B8, L=262,144 (65,536 groups), FP8 E4M3 KV, random pages, K=2,048 groups",
+    5: "decode B4 x 3 positions (base + 2 drafts), L0=131,072+r, Hq24/Hkv2, FP8 KV, K=1,024",
+}
+
+
+def algorithmic_bytes(wl) -> dict:
+    """Bytes a step must move at minimum: the k̂ of every complete group, the
+    K/V rows of every selected token, indexer/attention queries, outputs
+    and page-table entries read."""
+    g = wl.geom
+    esize = 1 if g["kv_dtype"] == 1 else 2
+    kv_row = 2 * g["num_kv_heads"] * g["head_dim"] * esize  # K + V of one token
+    Q = wl.q_per_req
+    khat = scores = pt = pt_score = kv = 0
+    for L in wl.ctx_lens.tolist():
+        G = L // 4
+        khat += G * 8 * 64 * 4                    # one 2 KiB fp32 k̂ per complete group
+        scores += G * 4                           # one fp32 score written per group
+        pt_score += (G + 15) // 16 * 4            # page ids read by the indexer
+        pt += (L + Q - 1 + 63) // 64 * 4          # page ids of the request
+        sel = 4 * min(g["topk_groups"], G) + (L + Q - 1 - 4 * G)
+        kv += sel * kv_row                        # K and V rows of the selected tokens
+    B = wl.batch
+    idx_q = B * (8 * 64 * 4 + 8 * 4)              # q_idx + w_idx
+    attn_io = B * Q * g["num_q_heads"] * g["head_dim"] * (2 + 4)  # bf16 q in, fp32 out
+    return dict(khat=khat, kv=kv, scores=scores, page_table=pt,
+                step=khat + kv + pt + idx_q + attn_io,
+                score_kernel=khat + scores + pt_score + idx_q)
+
+
+def source_digest(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "learned_sparse_attention_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.counters.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_digest") != digest:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
+    """The oracle, unchanged, on this host: full decode steps of a bounded
+    subset of requests, scaled to layer-steps/s of the whole batch."""
+    import oracle
+    reps, t_total, rows_done = 0, 0.0, 0
+    b = 0
+    while t_total < budget_s and reps < 64:
+        t0 = time.perf_counter()
+        oracle.decode(wl, rows=[b])
+        t_total += time.perf_counter() - t0
+        rows_done += 1
+        reps += 1
+        b = (b + 1) % wl.batch
+    per_request = t_total / rows_done
+    return {"value": 1.0 / (per_request * wl.batch), "unit": "layer-steps/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{rows_done} of the {wl.batch} requests of one step, run one at a time "
+                      f"({t_total:.1f} s), scaled to the full batch"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the QSA layer step is not sharded "
+              "here); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import learned_sparse_attention_amd as qsa
+    import workload
+    from tests import qsa_gpu as H
+
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    wl = workload.config(args.config)
+    t_gen = time.perf_counter() - t0
+    d = H.to_dev(wl, dev)
+    g = wl.geom
+    B, Q = wl.batch, wl.q_per_req
+    out = torch.empty((B, Q, g["num_q_heads"], g["head_dim"]), dtype=torch.float32, device=dev)
+    ws = torch.empty(qsa.decode_workspace_size(g, B, Q, wl.max_ctx), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        qsa.qsa_decode(g, d["k"], d["v"], d["khat"], d["pt"], d["ctx"], d["q_idx"], d["w_idx"],
+                       d["q"], wl.max_ctx, q_per_req=Q, out=out, workspace=ws,
+                       num_pages=wl.num_pages)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # dominant kernel alone: the indexer GEMV (one launch per call), timed
+    # with events on the current stream, which is the stream it runs on
+    sc = torch.empty((B, wl.max_ctx // 4), dtype=torch.float32, device=dev)
+
+    def score():
+        qsa.qsa_index_score(g, d["khat"], d["pt"], None, d["ctx"], d["q_idx"], d["w_idx"],
+                            wl.max_ctx - (Q - 1), out_scores=sc, num_pages=wl.num_pages)
+
+    for _ in range(args.warmup):
+        score()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        score()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_score = e0.elapsed_time(e1) / args.steps
+
+    ab = algorithmic_bytes(wl)
+    score_gbs = ab["score_kernel"] / (ms_score * 1e-3) / 1e9
+    step_gbs = ab["step"] / (ms_step * 1e-3) / 1e9
+    wname = f"cfg{args.config}"
+    digest = source_digest("index_score.hip", "qsa_device.h")
+    traffic = measured_traffic("index_score_gemv", wname, digest)
+
+    result = {
+        "metric": "QSA decode layer-steps/sec (B8, 256K ctx) + achieved HBM GB/s vs peak",
+        "value": 1000.0 / ms_step,
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded SplitMix64/Box-Muller; N(0,1) KV quantised to FP8 E4M3 "
+                "with per-tensor scale, N(0,1) q and k̂, U(0,1) w)",
+        "config": {"workload": CONFIG_NAMES[args.config], "batch": B, "q_per_req": Q,
+                   "ctx_lens": [int(x) for x in wl.ctx_lens[:8]], "topk_groups": g["topk_groups"],
+                   "num_q_heads": g["num_q_heads"], "num_kv_heads": g["num_kv_heads"],
+                   "head_dim": g["head_dim"], "kv": "fp8_e4m3" if g["kv_dtype"] else "bf16",
+                   "seed": wl.seed},
+        "roofline": {"kernel": "index_score_gemv_kernel", "bound": "hbm",
+                     "achieved": score_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": score_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": ab["score_kernel"],
+                     "ms_per_launch": ms_score},
+        "step_roofline": {"bound": "hbm", "algorithmic_bytes": ab["step"],
+                          "achieved": step_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": step_gbs / HBM_PEAK_GBS},
+        "gen_seconds": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

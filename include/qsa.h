@@ -140,6 +140,20 @@ size_t qsa_decode_workspace_size(const qsa_geometry* g, int32_t batch,
 size_t qsa_prefill_workspace_size(const qsa_geometry* g, int32_t n_q,
                                   int32_t max_ctx);
 
+/* Indexer scores only (step 1 above), fp32, for independent query rows:
+ * the decode-time GEMV over the paged k̂.  No workspace.
+ *
+ *   row_req   nullable [n_rows] int32: page-table row of each query row;
+ *             NULL means row r uses page-table row r.
+ *   row_len, q_idx, w_idx, max_ctx: as for qsa_index_topk.
+ *   out_scores [n_rows, max_ctx / ratio] f32; entries g >= floor(L/4) are
+ *             -inf, and so are groups on out-of-range pages.
+ */
+qsa_status qsa_index_score(const qsa_geometry* g, const qsa_paged_cache* cache,
+                           int32_t n_rows, int32_t max_ctx, const int32_t* row_req,
+                           const int32_t* row_len, const float* q_idx,
+                           const float* w_idx, float* out_scores, void* stream);
+
 /* Indexer score + exact top-K for independent query rows (steps 1-2 above),
  * fp32 arithmetic (a GEMV per row over the paged k̂).
  *

@@ -18,7 +18,7 @@ import math
 import os
 
 __all__ = ["QSAError", "load", "validate", "token_width", "index_topk_workspace_size",
-           "decode_workspace_size", "prefill_workspace_size", "qsa_index_topk", "qsa_decode",
+           "decode_workspace_size", "prefill_workspace_size", "qsa_index_score", "qsa_index_topk", "qsa_decode",
            "qsa_prefill", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsa.so")
@@ -74,6 +74,8 @@ def load():
             f = getattr(L, n)
             f.restype = sz
             f.argtypes = args
+        L.qsa_index_score.restype = ctypes.c_int
+        L.qsa_index_score.argtypes = [G, C, i32, i32, vp, vp, vp, vp, vp, vp]
         L.qsa_index_topk.restype = ctypes.c_int
         L.qsa_index_topk.argtypes = [G, C, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.qsa_decode.restype = ctypes.c_int
@@ -149,6 +151,24 @@ def decode_workspace_size(geom: dict, batch: int, q_per_req: int, max_ctx: int) 
 
 def prefill_workspace_size(geom: dict, n_q: int, max_ctx: int) -> int:
     return load().qsa_prefill_workspace_size(ctypes.byref(_geom(geom)), n_q, max_ctx)
+
+
+def qsa_index_score(geom, khat, page_table, row_req, row_len, q_idx, w_idx, max_ctx,
+                    out_scores=None, num_pages=None):
+    """Indexer scores only (fp32 GEMV).  row_req may be None (row r uses
+    page-table row r).  Returns out_scores [n_rows, max_ctx // 4]."""
+    import torch
+    dev = q_idx.device
+    n = int(row_len.shape[0])
+    if out_scores is None:
+        out_scores = torch.empty((n, max_ctx // 4), dtype=torch.float32, device=dev)
+    g = _geom(geom)
+    c, keep = _cache(None, None, khat, page_table, num_pages)
+    args = [_c(row_req), _c(row_len), _c(q_idx), _c(w_idx)]
+    code = load().qsa_index_score(ctypes.byref(g), ctypes.byref(c), n, int(max_ctx),
+                                  *(_ptr(t) for t in args), _ptr(out_scores), _stream(dev))
+    _check("qsa_index_score", code)
+    return out_scores
 
 
 def qsa_index_topk(geom, khat, page_table, row_req, row_len, q_idx, w_idx, max_ctx,

@@ -168,6 +168,24 @@ size_t qsa_prefill_workspace_size(const qsa_geometry* g, int32_t n_q, int32_t ma
   return rows_layout(g, n_q, max_ctx).total;
 }
 
+qsa_status qsa_index_score(const qsa_geometry* g, const qsa_paged_cache* cache, int32_t n_rows,
+                           int32_t max_ctx, const int32_t* row_req, const int32_t* row_len,
+                           const float* q_idx, const float* w_idx, float* out_scores,
+                           void* stream) {
+  qsa_status st = qsa_validate(g);
+  if (st != QSA_OK) return st;
+  if (n_rows < 0 || max_ctx < 1 || max_ctx > kCapacity || !cache_ok(cache, false))
+    return QSA_ERR_INVALID_ARG;
+  if (max_ctx > cache->max_pages * kPage) return QSA_ERR_INVALID_ARG;
+  if (n_rows == 0) return QSA_OK;
+  if (!row_len || !q_idx || !w_idx || !out_scores) return QSA_ERR_INVALID_ARG;
+  QSA_HIP(launch_index_score_gemv(cache->khat, cache->page_table, cache->max_pages,
+                                  cache->num_pages, n_rows, row_req, row_len, 0, 0, max_ctx,
+                                  q_idx, w_idx, out_scores, gstride_of(max_ctx), false,
+                                  (hipStream_t)stream));
+  return QSA_OK;
+}
+
 qsa_status qsa_index_topk(const qsa_geometry* g, const qsa_paged_cache* cache, int32_t n_rows,
                           int32_t max_ctx, const int32_t* row_req, const int32_t* row_len,
                           const float* q_idx, const float* w_idx, int32_t* out_groups,
