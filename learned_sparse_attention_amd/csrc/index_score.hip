@@ -9,8 +9,9 @@
 // The work is a stream over k̂ (2 KiB per group, 0.5 flop per byte), so the
 // kernel is built for HBM bandwidth, not arithmetic:
 //   - one wavefront consumes one 32 KiB k̂ page (16 groups) with fully
-//     coalesced 16-byte loads: lane l reads float4 #l of each 1 KiB half of
-//     a group, i.e. heads l/16 and 4 + l/16, dims 4*(l%16) .. +3;
+//     coalesced, non-temporal 16-byte loads (k̂ is read once per step):
+//     lane l reads float4 #l of each 1 KiB half of a group, i.e. heads l/16
+//     and 4 + l/16, dims 4*(l%16) .. +3;
 //   - each lane keeps the matching 8 query values and 2 weights in
 //     registers for the whole launch;
 //   - per-head dot products finish with DPP row reductions (a DPP row is
@@ -76,8 +77,8 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_gemv_kernel(
         float v[kGroupsPerPage];
 #pragma unroll
         for (int g = 0; g < kGroupsPerPage; ++g) {
-          float4 x0 = base[g * 128 + lane];
-          float4 x1 = base[g * 128 + 64 + lane];
+          float4 x0 = stream_load(base + g * 128 + lane);
+          float4 x1 = stream_load(base + g * 128 + 64 + lane);
           if (kRound) { x0 = round4(x0); x1 = round4(x1); }
           float p0 = row16_sum(dot4(x0, qa));
           float p1 = row16_sum(dot4(x1, qb));

@@ -38,7 +38,7 @@ int groups_per_split(const qsa_geometry* g, int batch, int q_per_req) {
 
 struct DecodeLayout {
   int gps, n_splits, gstride;
-  size_t off_scores, off_sel, off_partial, total;
+  size_t off_scores, off_sel, off_partial, off_topk, total;
 };
 
 DecodeLayout decode_layout(const qsa_geometry* g, int batch, int q_per_req, int max_ctx) {
@@ -55,13 +55,15 @@ DecodeLayout decode_layout(const qsa_geometry* g, int batch, int q_per_req, int 
   d.off_partial = off;
   off += align_up(sizeof(float) * (size_t)batch * g->num_kv_heads * d.n_splits * rows *
                   (2 + kHeadDim));
+  d.off_topk = off;
+  off += align_up(topk_workspace_bytes(batch, d.gstride));
   d.total = off;
   return d;
 }
 
 struct RowsLayout {
   int gstride;
-  size_t off_scores, off_sel, total;
+  size_t off_scores, off_sel, off_topk, total;
 };
 
 RowsLayout rows_layout(const qsa_geometry* g, int n_rows, int max_ctx) {
@@ -72,6 +74,8 @@ RowsLayout rows_layout(const qsa_geometry* g, int n_rows, int max_ctx) {
   off += align_up(sizeof(float) * (size_t)n_rows * r.gstride);
   r.off_sel = off;
   off += align_up(sizeof(int32_t) * (size_t)n_rows * g->topk_groups);
+  r.off_topk = off;
+  off += align_up(topk_workspace_bytes(n_rows, r.gstride));
   r.total = off;
   return r;
 }
@@ -198,14 +202,14 @@ qsa_status qsa_index_topk(const qsa_geometry* g, const qsa_paged_cache* cache, i
   if (n_rows == 0) return QSA_OK;
   if (!row_req || !row_len || !q_idx || !w_idx || !out_groups) return QSA_ERR_INVALID_ARG;
   const RowsLayout lay = rows_layout(g, n_rows, max_ctx);
-  if (!out_scores && (st = ws_ok(ws, ws_bytes, lay.off_sel)) != QSA_OK) return st;
+  if ((st = ws_ok(ws, ws_bytes, lay.total)) != QSA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   float* scores = out_scores ? out_scores : (float*)((char*)ws + lay.off_scores);
   QSA_HIP(launch_index_score_gemv(cache->khat, cache->page_table, cache->max_pages,
                                   cache->num_pages, n_rows, row_req, row_len, 0, 0, max_ctx,
                                   q_idx, w_idx, scores, lay.gstride, false, s));
   QSA_HIP(launch_topk(scores, lay.gstride, n_rows, row_len, 0, max_ctx, g->topk_groups,
-                      out_groups, s));
+                      out_groups, (char*)ws + lay.off_topk, s));
   return QSA_OK;
 }
 
@@ -235,7 +239,7 @@ qsa_status qsa_decode(const qsa_geometry* g, const qsa_paged_cache* cache, int32
                                   max_ctx - (q_per_req - 1), q_idx, w_idx, scores, lay.gstride,
                                   false, s));
   QSA_HIP(launch_topk(scores, lay.gstride, batch, ctx_lens, 0, max_ctx - (q_per_req - 1),
-                      g->topk_groups, sel, s));
+                      g->topk_groups, sel, w + lay.off_topk, s));
   AttnArgs a = attn_args(g, cache);
   a.sel = sel;
   a.ctx_lens = ctx_lens;
@@ -276,7 +280,7 @@ qsa_status qsa_prefill(const qsa_geometry* g, const qsa_paged_cache* cache, int3
                                   cache->num_pages, n_q, nullptr, nullptr, req, first_pos,
                                   max_ctx, q_idx, w_idx, scores, lay.gstride, true, s));
   QSA_HIP(launch_topk(scores, lay.gstride, n_q, nullptr, first_pos, max_ctx, g->topk_groups, sel,
-                      s));
+                      w + lay.off_topk, s));
   AttnArgs a = attn_args(g, cache);
   a.sel = sel;
   a.first_pos = first_pos;

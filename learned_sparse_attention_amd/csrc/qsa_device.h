@@ -53,6 +53,19 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Streaming 16-byte load: data read once per launch is fetched non-temporally
+// so it does not displace reused lines (measured ~12% more HBM read
+// bandwidth than plain loads on MI355X for multi-GiB streams).
+typedef float qsa_f4v __attribute__((ext_vector_type(4)));
+typedef unsigned int qsa_u4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 stream_load(const float4* p) {
+  const qsa_f4v v = __builtin_nontemporal_load(reinterpret_cast<const qsa_f4v*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ qsa_u4v stream_load_u4(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const qsa_u4v*>(p));
+}
+
 // Wave-wide helpers ---------------------------------------------------------
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -28,9 +28,12 @@ hipError_t launch_index_score_prefill(const float* khat, const int32_t* page_tab
 
 // Exact top-K of each row: candidates g < G(row) where G = floor(L/4) for
 // L = row_len[row] in [0, max_ctx] (else G = 0); when row_len is null,
-// L = first_pos + row + 1.  out is [n_rows, K] ascending, -1 padded.
+// L = first_pos + row + 1.  out is [n_rows, K] ascending, -1 padded.  ws
+// (256-byte aligned, topk_workspace_bytes) holds candidates of long rows.
+size_t topk_workspace_bytes(int n_rows, int gstride);
 hipError_t launch_topk(const float* scores, int gstride, int n_rows, const int32_t* row_len,
-                       int first_pos, int max_ctx, int K, int32_t* out, hipStream_t stream);
+                       int first_pos, int max_ctx, int K, int32_t* out, void* ws,
+                       hipStream_t stream);
 
 struct AttnArgs {
   const void* k;

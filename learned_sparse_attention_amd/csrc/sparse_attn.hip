@@ -369,30 +369,38 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(AttnArgs a) 
 }
 
 // Merge split partials: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+// Thread s first fetches split s's (m, l) so all splits are read at once;
+// then thread d sums the accumulators with independent loads.
+constexpr int kMaxSplits = kHeadDim;
 __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restrict__ partial,
                                                            int n_splits, int Hq, int Hkv, int Q,
                                                            float v_scale, float* __restrict__ out) {
+  __shared__ float fac[kMaxSplits];
+  __shared__ float red[kHeadDim / kWave];
   const int h = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int gq = Hq / Hkv, kvh = h / gq, r = j * gq + (h % gq);
   const int R = Q * gq;
-  const float* p = partial + ((size_t)(b * Hkv + kvh) * n_splits) * R * (2 + kHeadDim) +
-                   (size_t)r * (2 + kHeadDim);
   const size_t split_stride = (size_t)R * (2 + kHeadDim);
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, p[s * split_stride]);
-  float num = 0.0f, den = 0.0f;
-  const int d = threadIdx.x;
-  if (M != -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const float* ps = p + s * split_stride;
-      const float m = ps[0];
-      if (m == -INFINITY) continue;
-      const float f = exp2f(m - M);
-      den += f * ps[1];
-      num += f * ps[2 + d];
-    }
-  }
-  out[(((size_t)b * Q + j) * Hq + h) * kHeadDim + d] = den > 0.0f ? num * (v_scale / den) : 0.0f;
+  const float* p = partial + ((size_t)(b * Hkv + kvh) * n_splits) * split_stride +
+                   (size_t)r * (2 + kHeadDim);
+  const int t = threadIdx.x, lane = t & (kWave - 1), wid = t / kWave;
+  const float m = t < n_splits ? p[t * split_stride] : -INFINITY;
+  const float l = t < n_splits ? p[t * split_stride + 1] : 0.0f;
+  float M = wave_max(m);
+  if (lane == 0) red[wid] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float f = (m == -INFINITY) ? 0.0f : exp2f(m - M);
+  if (t < n_splits) fac[t] = f;
+  __syncthreads();
+  float den = wave_sum(f * l);
+  if (lane == 0) red[wid] = den;  // (every thread has read red[] above)
+  __syncthreads();
+  den = (red[0] + red[1]) + (red[2] + red[3]);
+  float num = 0.0f;
+#pragma unroll 8
+  for (int s = 0; s < n_splits; ++s) num += fac[s] * p[s * split_stride + 2 + t];
+  out[(((size_t)b * Q + j) * Hq + h) * kHeadDim + t] = den > 0.0f ? num * (v_scale / den) : 0.0f;
 }
 
 // Token lists: slot i < 4*n_valid -> 4*sel[i/4] + i%4; then the extra range.
@@ -422,6 +430,7 @@ size_t attn_smem_bytes(int NB, int stream_cap) {
 
 template <bool kFp8, int NB>
 hipError_t launch_decode_nb(const AttnArgs& a, hipStream_t stream) {
+  if (a.n_splits > kMaxSplits) return hipErrorInvalidValue;
   const int cap = 4 * a.groups_per_split + 3 + (a.q_per_req - 1);
   const size_t smem = attn_smem_bytes(NB, cap);
   const int rows = a.q_per_req * (a.Hq / a.Hkv);

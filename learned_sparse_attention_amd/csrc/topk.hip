@@ -1,5 +1,5 @@
 // topk.hip — exact top-K of the indexer scores with a lowest-index
-// tie-break, one workgroup per query row.
+// tie-break.
 //
 // The TensorRT-LLM QSASparseAttentionConfig reference names an exact radix
 // top-K as the default selector over the compressed groups
@@ -7,34 +7,47 @@
 // ranks by (score descending, group index ascending).  Output per row: the
 // min(K, G) selected group ids in ascending order, then -1.
 //
-// Design (gfx950, one workgroup of 256..1,024 threads per row):
-//   * Thread t of NT owns elements t, t + NT, t + 2NT, ... so every load of
-//     the score row is fully coalesced; the keys stay in registers for the
-//     whole kernel (65,536 groups = 262,144 tokens use 512 threads x 128).
-//   * Pass 1 bins the finite scores linearly between their min and max
-//     (4,096 LDS bins).  The bin function is monotone in the score, so all
-//     elements above the bin that holds the K-th element are selected and
-//     only that bin's members stay candidates — usually a handful, and the
-//     histogram spreads LDS atomics across many bins.
-//   * Three exact radix passes over the order-preserving 32-bit keys of the
-//     remaining candidates (11 + 11 + 10 bits) find the K-th key T exactly
-//     and how many elements equal to T must be taken.
-//   * Compaction in index order uses wave ballots: per (element slot,
-//     wave) popcounts are scanned once across the block, which gives every
-//     element its rank among equal keys and its output position, so the
-//     output is ascending without any sort.
+// Rows longer than kDirect groups (decode at long context: up to 65,536
+// groups per row, only a handful of rows) are spread over many compute
+// units in two launches:
+//   extract  one workgroup per 4,096-group slice.  Every slice of a row
+//            derives the same pruning threshold ("guess") from 512 evenly
+//            spaced sample scores of the row: an exact radix select of the
+//            r-th largest sample, with r = the sample rank of K plus four
+//            standard deviations of its sampling error, so the guess lies
+//            below the K-th largest score with overwhelming probability.
+//            The slice then writes every score >= guess (typically ~6.6% at
+//            K/G = 1/32) with its index to its own region of the workspace.
+//   finish   one workgroup per row gathers the candidates (~4K), finds the
+//            K-th key T exactly with four 8-bit radix passes over the key
+//            offsets from the smallest candidate, marks key > T and key == T
+//            in LDS bitmaps, and emits ascending indices, copies of T in
+//            index order, through a block scan of bitmap popcounts.
+//            If a slice overflowed or fewer than K candidates survived (the
+//            guess missed), the row is re-ranked exactly from the full score
+//            row instead, so the result never depends on the sample.
+// Shorter rows (up to 16,384 groups, e.g. prefill queries: thousands of
+// rows) skip the extract step: every group is a candidate of the finish
+// step.
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
 namespace qsa {
 namespace {
 
-constexpr int kBins = 4096;
-constexpr int kSlots = 1024;  // (element slot, wave) pairs: E * waves <= 1024
+constexpr int kSlice = 4096;       // groups per extract workgroup
+constexpr int kSliceCap = 1024;    // candidate slots per slice
+constexpr int kSample = 512;       // sample scores per row
+constexpr int kDirect = 16384;     // rows up to this length skip extraction
+constexpr int kMaxGroups = 65536;  // 262,144 tokens / 4
+constexpr int kMaxSlices = kMaxGroups / kSlice;
+constexpr int kFinishThreads = 1024;
+constexpr int kExtractThreads = 256;
+constexpr int kBins = 4096;        // fallback value-linear bins
 
 // Inclusive prefix sum across the 64 lanes of a wavefront with DPP: four
 // row shifts build 16-lane prefix sums, then row broadcasts of lanes 15 and
-// 31 carry them into the next rows.  No address registers are needed.
+// 31 carry them into the next rows.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
   x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
@@ -43,6 +56,18 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
   x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return x;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+  return v;
 }
 
 // Exclusive prefix sum over the block of NT threads; tmp holds NT/64 + 1
@@ -65,102 +90,128 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp) {
   return r;
 }
 
-// In-place exclusive scan of cnt[0..kSlots) by NT threads (each owns
-// kSlots / NT consecutive entries).
-template <int NT>
-__device__ __forceinline__ void scan_slots(uint32_t* cnt, uint32_t* tmp) {
-  constexpr int C = kSlots / NT;
-  const int tid = threadIdx.x;
-  uint32_t v[C], local = 0;
-#pragma unroll
-  for (int c = 0; c < C; ++c) { v[c] = cnt[tid * C + c]; local += v[c]; }
-  uint32_t run = block_excl_scan<NT>(local, tmp);
-#pragma unroll
-  for (int c = 0; c < C; ++c) { cnt[tid * C + c] = run; run += v[c]; }
-  __syncthreads();
-}
-
-// Given per-bin counts in hist[0..nbins), find the bin b holding the
+// Wave-level search of a 256-bin histogram for the bin holding the
 // need-th largest element: count(bins > b) < need <= count(bins >= b).
-// Writes b and need - count(bins > b) to out[0], out[1].
-template <int NT>
-__device__ __forceinline__ void find_threshold_bin(const uint32_t* hist, int nbins, uint32_t need,
-                                                   uint32_t* tmp, int* out) {
-  const int per = nbins / NT;  // bins per thread, >= 1
-  const int hi = nbins - per * (int)threadIdx.x;  // thread t covers [hi - per, hi)
-  uint32_t local = 0;
-  for (int i = 0; i < per; ++i) local += hist[hi - 1 - i];
-  uint32_t above = block_excl_scan<NT>(local, tmp);
-  if (above < need && need <= above + local) {
-    for (int i = 0; i < per; ++i) {
-      const uint32_t c = hist[hi - 1 - i];
-      if (above + c >= need) {
-        out[0] = hi - 1 - i;
-        out[1] = (int)(need - above);
-        break;
-      }
-      above += c;
-    }
+// Lane l owns bins [252 - 4l, 256 - 4l).  Every lane gets b and
+// need - count(bins > b).
+__device__ __forceinline__ void wave_find256(const uint32_t* hist, uint32_t need, uint32_t* bin,
+                                             uint32_t* rem) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int lo = 252 - 4 * lane;
+  const uint4 v = *reinterpret_cast<const uint4*>(hist + lo);
+  const uint32_t local = (v.x + v.y) + (v.z + v.w);
+  const uint32_t incl = wave_incl_scan(local);
+  const bool mine = incl - local < need && need <= incl;
+  uint32_t r = need - (incl - local);
+  uint32_t b = lo;
+  if (r <= v.w) b = lo + 3;
+  else if ((r -= v.w) <= v.z) b = lo + 2;
+  else if ((r -= v.z) <= v.y) b = lo + 1;
+  else r -= v.y;
+  const uint64_t m = __ballot(mine);
+  const int src = m ? __ffsll((unsigned long long)m) - 1 : 0;
+  *bin = (uint32_t)__shfl((int)b, src, kWave);
+  *rem = (uint32_t)__shfl((int)r, src, kWave);
+}
+
+// Block-level 256-bin search (wave 0 searches; result through sh).
+__device__ __forceinline__ void block_find256(const uint32_t* hist, uint32_t need, int* sh,
+                                              uint32_t* bin, uint32_t* rem) {
+  if (threadIdx.x < kWave) {
+    uint32_t b, r;
+    wave_find256(hist, need, &b, &r);
+    if (threadIdx.x == 0) { sh[0] = (int)b; sh[1] = (int)r; }
   }
+  __syncthreads();
+  *bin = (uint32_t)sh[0];
+  *rem = (uint32_t)sh[1];
   __syncthreads();
 }
 
-// Empty register fence: tells the compiler the keys may have changed, so
-// per-element predicates are recomputed in each pass instead of being kept
-// alive across passes.
-template <int E>
-__device__ __forceinline__ void fence_keys(uint32_t (&key)[E]) {
+// r-th largest of 8 keys per lane of one wave (512 keys), exact: four
+// 8-bit radix passes with an LDS histogram owned by this wave alone (LDS
+// operations of one wave execute in order, so no barrier is needed).
+__device__ uint32_t wave_select_rth(const uint32_t (&k)[8], uint32_t r, uint32_t* hist) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t prefix = 0, pmask = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) asm volatile("" : "+v"(key[e]));
+  for (int p = 0; p < 4; ++p) {
+    const int s = 24 - 8 * p;
+    *reinterpret_cast<uint4*>(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((k[i] & pmask) == prefix) atomicAdd(&hist[(k[i] >> s) & 255u], 1u);
+    __builtin_amdgcn_wave_barrier();
+    uint32_t b;
+    wave_find256(hist, r, &b, &r);
+    __builtin_amdgcn_wave_barrier();
+    prefix |= b << s;
+    pmask |= 255u << s;
+  }
+  return prefix;
 }
 
-// NT threads, E keys per thread; element e of thread t is group e*NT + t.
-template <int NT, int E>
-__global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores, int gstride,
-                                                  const int32_t* __restrict__ row_len,
-                                                  int first_pos, int max_ctx, int K,
-                                                  int32_t* __restrict__ out) {
+// Exact threshold among M candidate keys per thread (0 = empty slot):
+// the need-th largest key T and how many copies of T are taken.  Radix
+// passes of 8 bits over the offsets key - kmin, starting at the highest
+// bit where the candidates differ.
+template <int NT, int M>
+__device__ uint32_t candidate_threshold(const uint32_t (&key)[M], uint32_t need, uint32_t* hist,
+                                        uint32_t* tmp, int* sh, uint32_t* take_eq) {
   constexpr int NW = NT / kWave;
-  static_assert(E * NW <= kSlots, "slot table too small");
-  __shared__ uint32_t hist[kBins + 1];  // + dummy bin for slots past the row
-  __shared__ uint32_t cnt_eq[kSlots];
-  __shared__ uint32_t cnt_sel[kSlots];
-  __shared__ uint32_t tmp[NW + 1];
-  __shared__ float red[2][NW];
-  __shared__ int thr[2];
-
-  const int row = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1), wid = tid / kWave;
-  const int L = row_len ? row_len[row] : first_pos + row + 1;
-  int G = (L >= 0 && L <= max_ctx) ? L / kRatio : 0;
-  if (G > gstride) G = gstride;
-  int32_t* orow = out + (size_t)row * K;
-
-  if (G <= K) {  // every complete group is kept
-    for (int i = tid; i < K; i += NT) orow[i] = (i < G) ? i : -1;
-    return;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    if (key[m]) { kmin = min(kmin, key[m]); kmax = max(kmax, key[m]); }
   }
-
-  // Unconditional loads (clamped to the row) so all are in flight at once;
-  // elements at or past G become key 0 (not a candidate).
-  const float* srow = scores + (size_t)row * gstride;
-  const int g_rel = G - tid;  // element e is a candidate iff e * NT < g_rel
-  const int last = gstride - 1 - tid;
-  uint32_t key[E];
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) { tmp[wid] = kmin; tmp[NW + wid] = kmax; }
+  __syncthreads();
+  kmin = tmp[0]; kmax = tmp[NW];
+  for (int w = 1; w < NW; ++w) { kmin = min(kmin, tmp[w]); kmax = max(kmax, tmp[NW + w]); }
+  __syncthreads();
+  const uint32_t span = kmax - kmin;
+  int nbits = span ? 32 - __clz(span) : 0;  // offsets fit in nbits bits
+  uint32_t prefix = 0, pmask = 0;           // over offsets
+  while (nbits > 0) {
+    const int s = nbits > 8 ? nbits - 8 : 0;
+    const uint32_t dmask = (1u << (nbits - s)) - 1u;
+    for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+    __syncthreads();
 #pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = __float_as_uint(srow[tid + min(e * NT, last)]);
-  fence_keys(key);
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    key[e] = (e * NT < g_rel) ? score_key(__uint_as_float(key[e])) : 0u;
+    for (int m = 0; m < M; ++m) {
+      const uint32_t off = key[m] - kmin;
+      if (key[m] && (off & pmask) == prefix) atomicAdd(&hist[(off >> s) & dmask], 1u);
+    }
+    __syncthreads();
+    uint32_t d;
+    block_find256(hist, need, sh, &d, &need);
+    prefix |= d << s;
+    pmask |= dmask << s;
+    nbits = s;
+  }
+  *take_eq = need;
+  return kmin + prefix;
+}
 
-  // ---- min / max of the finite scores
+// Exact threshold over all G scores of a row, streamed from memory in
+// every pass (the rare path taken when the pruning guess misses): the
+// need-th largest key T and how many copies of T are taken.  Keys are
+// ranked by value-linear bins first (4,096 bins between min and max of the
+// finite scores; monotone in the score), then by three radix digits of the
+// keys inside the bin that holds the need-th one.
+template <int NT>
+__device__ uint32_t exact_threshold_stream(const float* srow, int G, uint32_t need, uint32_t* hist,
+                                           float* red, int* sh, uint32_t* take_eq) {
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const float v = key_value(key[e]);
-    const bool ok = (key[e] != 0u) && (fabsf(v) < INFINITY);
+  for (int i = tid; i < G; i += NT) {
+    const float v = srow[i];
+    const bool ok = fabsf(v) < INFINITY;
     mn = fminf(mn, ok ? v : INFINITY);
     mx = fmaxf(mx, ok ? v : -INFINITY);
   }
@@ -169,41 +220,54 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     mn = fminf(mn, __shfl_xor(mn, o, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
   }
-  if (lane == 0) { red[0][wid] = mn; red[1][wid] = mx; }
-  for (int i = tid; i <= kBins; i += NT) hist[i] = 0u;
+  if (lane == 0) { red[wid] = mn; red[NW + wid] = mx; }
+  for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
   __syncthreads();
-  mn = red[0][0]; mx = red[1][0];
-  for (int w = 1; w < NW; ++w) { mn = fminf(mn, red[0][w]); mx = fmaxf(mx, red[1][w]); }
+  mn = red[0]; mx = red[NW];
+  for (int w = 1; w < NW; ++w) { mn = fminf(mn, red[w]); mx = fmaxf(mx, red[NW + w]); }
+  __syncthreads();
   float scale = 0.0f;
   if (mx > mn) {
     scale = (float)kBins / (mx - mn);
     if (!(scale < INFINITY)) scale = 0.0f;
   }
-
-  // ---- pass 1: value-linear bins (monotone in the score)
   // Branch-free and monotone non-decreasing in the score: -inf -> 0, values
   // at or above mx -> kBins - 1 (a NaN product, only possible when
-  // scale == 0, also lands in bin 0 together with every finite value).
+  // scale == 0, lands in bin 0 together with every finite value).
   auto bin_of = [&](uint32_t k) -> int {
     const float t = (key_value(k) - mn) * scale;
     return (int)fminf(fmaxf(t, 0.0f), (float)(kBins - 1));
   };
-  fence_keys(key);
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    // wave-uniform skip of slots past the row; stragglers count in a dummy bin
-    if (e * NT + wid * kWave < G) atomicAdd(&hist[key[e] ? bin_of(key[e]) : kBins], 1u);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int i = tid; i < G; i += NT) atomicAdd(&hist[bin_of(score_key(srow[i]))], 1u);
+  __syncthreads();
+  // bin holding the need-th largest: 16 coarse groups of 256 bins, then fine
+  if (tid < kWave) {
+    uint32_t above = 0;
+    int b = 0;
+    for (int grp = 15; grp >= 0; --grp) {
+      uint32_t c = 0;
+      for (int i = tid; i < 256; i += kWave) c += hist[grp * 256 + i];
+      c = wave_incl_scan(c);
+      c = (uint32_t)__shfl((int)c, kWave - 1, kWave);
+      if (above + c >= need) {
+        uint32_t bb, rr;
+        wave_find256(hist + grp * 256, need - above, &bb, &rr);
+        b = grp * 256 + (int)bb;
+        above = need - rr;
+        break;
+      }
+      above += c;
+    }
+    if (tid == 0) { sh[0] = b; sh[1] = (int)(need - above); }
   }
   __syncthreads();
-  find_threshold_bin<NT>(hist, kBins, (uint32_t)K, tmp, thr);
-  const int tb = thr[0];
-  uint32_t need = (uint32_t)thr[1];
+  const int tb = sh[0];
+  need = (uint32_t)sh[1];
+  __syncthreads();
 
-  // The keys whose bin is tb form one contiguous key range [lo, hi]
-  // (the bin function is monotone in the key between key(-inf) and
-  // key(+inf)); one thread finds its ends by bisection, so candidates are
-  // tested by two compares instead of re-binning every element.
+  // The keys whose bin is tb form one contiguous key range [lo, hi] (the
+  // bin function is monotone in the key between key(-inf) and key(+inf));
+  // one thread finds its ends by bisection.
   if (tid == 0) {
     const uint32_t kneg = score_key(-INFINITY), kpos = score_key(INFINITY);
     uint32_t a = kneg, b = kpos;  // smallest key with bin >= tb
@@ -216,119 +280,285 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
       const uint32_t m = c + (d - c + 1) / 2;
       if (bin_of(m) <= tb) c = m; else d = m - 1;
     }
-    thr[0] = (int)a;
-    thr[1] = (int)c;
+    sh[2] = (int)a;
+    sh[3] = (int)c;
   }
   __syncthreads();
-  uint32_t lo = (uint32_t)thr[0], hi = (uint32_t)thr[1];
-
-  // ---- passes 2-4: exact radix over the candidates' keys; each pass
-  // narrows [lo, hi] to the keys that share the chosen digit prefix
-  const int shifts[3] = {21, 10, 0};
-  const int widths[3] = {11, 11, 10};
-#pragma unroll
-  for (int p = 0; p < 3; ++p) {
-    const int sh = shifts[p];
-    const uint32_t dmask = (1u << widths[p]) - 1u;
-    const int nb = 1 << widths[p];
+  const uint32_t lo = (uint32_t)sh[2], hi = (uint32_t)sh[3];
+  __syncthreads();
+  // four 8-bit radix passes over the offsets k - lo of the keys in [lo, hi]
+  uint32_t prefix = 0, pmask = 0;
+  for (int p = 0; p < 4; ++p) {
+    const int s = 24 - 8 * p;
+    for (int i = tid; i < 256; i += NT) hist[i] = 0u;
     __syncthreads();
-    for (int i = tid; i < nb; i += NT) hist[i] = 0u;
-    __syncthreads();
-    fence_keys(key);
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if (key[e] >= lo && key[e] <= hi) atomicAdd(&hist[(key[e] >> sh) & dmask], 1u);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int i = tid; i < G; i += NT) {
+      const uint32_t k = score_key(srow[i]);
+      const uint32_t off = k - lo;
+      if (k >= lo && k <= hi && (off & pmask) == prefix) atomicAdd(&hist[(off >> s) & 255u], 1u);
     }
     __syncthreads();
-    find_threshold_bin<NT>(hist, nb, need, tmp, thr);
-    const uint32_t d = (uint32_t)thr[0];
-    need = (uint32_t)thr[1];
-    const uint32_t top = ~((dmask << sh) | ((1u << sh) - 1u));  // bits above the digit
-    const uint32_t base = (lo & top) | (d << sh);
-    lo = max(lo, base);
-    hi = min(hi, base | ((1u << sh) - 1u));
+    uint32_t d;
+    block_find256(hist, need, sh, &d, &need);
+    prefix |= d << s;
+    pmask |= 255u << s;
   }
-  const uint32_t prefix = lo;
-  const uint32_t T = prefix;  // the K-th largest key; take `need` of its copies
+  *take_eq = need;
+  return lo + prefix;
+}
 
-  // ---- compaction in index order.  Element e of thread t has index
-  // e * NT + t, so index order is (slot e, wave, lane): per (e, wave) ballot
-  // popcounts scanned across the block give each element its rank among
-  // the keys equal to T and then its output position.  Ballots are
-  // recomputed rather than stored.
-  const uint64_t lt = (1ull << lane) - 1ull;
-  fence_keys(key);
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint64_t eqb = __ballot(key[e] == T);
-    if (lane == 0) cnt_eq[e * NW + wid] = (uint32_t)__popcll(eqb);
+// ---------------------------------------------------------------------------
+// extract: one workgroup per (slice, row)
+
+__global__ __launch_bounds__(kExtractThreads) void topk_extract_kernel(
+    const float* __restrict__ scores, int gstride, const int32_t* __restrict__ row_len,
+    int first_pos, int max_ctx, int K, uint32_t* __restrict__ cand_val,
+    uint16_t* __restrict__ cand_idx, int32_t* __restrict__ cand_cnt) {
+  constexpr int NT = kExtractThreads, NW = NT / kWave;
+  constexpr int E4 = kSlice / (4 * NT);  // float4 chunks per thread
+  constexpr int kCW = kSliceCap / NW;    // slots per wave
+  __shared__ __attribute__((aligned(16))) uint32_t hist[256];
+  __shared__ uint32_t sval[kSliceCap];
+  __shared__ uint16_t sidx[kSliceCap];
+  __shared__ uint32_t wcnt[NW];
+  __shared__ float sguess;
+
+  const int slice = blockIdx.x, row = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int L = row_len ? row_len[row] : first_pos + row + 1;
+  int G = (L >= 0 && L <= max_ctx) ? L / kRatio : 0;
+  if (G > gstride) G = gstride;
+  const size_t slot0 = ((size_t)row * kMaxSlices + slice) * kSliceCap;
+  const int g0 = slice * kSlice;
+  if (G <= K || g0 >= G) {  // finish handles the row alone / empty slice
+    if (tid == 0) cand_cnt[row * kMaxSlices + slice] = 0;
+    return;
   }
-  for (int i = E * NW + tid; i < kSlots; i += NT) cnt_eq[i] = 0u;
+  const float* srow = scores + (size_t)row * gstride;
+
+  // slice loads (in flight while wave 0 derives the guess)
+  uint32_t v[4 * E4];
+#pragma unroll
+  for (int e = 0; e < E4; ++e) {
+    const int c0 = g0 + 4 * (e * NT + tid);
+    if (((reinterpret_cast<uintptr_t>(srow) & 15u) == 0u) && c0 + 3 < G) {
+      const float4 f = *reinterpret_cast<const float4*>(srow + c0);
+      v[4 * e] = __float_as_uint(f.x); v[4 * e + 1] = __float_as_uint(f.y);
+      v[4 * e + 2] = __float_as_uint(f.z); v[4 * e + 3] = __float_as_uint(f.w);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[4 * e + j] = c0 + j < G ? __float_as_uint(srow[c0 + j]) : 0x7FC00000u;  // NaN: never kept
+    }
+  }
+
+  if (wid == 0) {
+    uint32_t sk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int si = (int)(((long long)(lane + kWave * i) * G) / kSample);
+      sk[i] = score_key(srow[si]);
+    }
+    const int r0 = (int)(((long long)kSample * K + G - 1) / G);
+    int r = r0 + 4 * (int)ceilf(sqrtf((float)r0)) + 4;
+    if (r > kSample) r = kSample;
+    const uint32_t gk = wave_select_rth(sk, (uint32_t)r, hist);
+    if (lane == 0) sguess = key_value(gk);
+  }
   __syncthreads();
-  scan_slots<NT>(cnt_eq, tmp);
-  // Per-slot bases are wave-uniform: lane l holds the base of slot l (and
-  // l + 64), and each slot reads it back with v_readlane into a scalar.
-  constexpr int NV = (E + kWave - 1) / kWave;
-  uint32_t eq_base[NV], sel_base[NV];
+  const float guess = sguess;
+
+  // keep scores >= guess, each wave in its own region, in order
+  uint32_t run = 0;
 #pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    const int e = v * kWave + lane;
-    eq_base[v] = e < E ? cnt_eq[e * NW + wid] : 0u;
+  for (int e = 0; e < 4 * E4; ++e) {
+    const bool pred = __uint_as_float(v[e]) >= guess;
+    const uint64_t mask = __ballot(pred);
+    const uint32_t pos = run + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+    if (pred && pos < (uint32_t)kCW) {
+      sval[wid * kCW + pos] = v[e];
+      sidx[wid * kCW + pos] = (uint16_t)(g0 + 4 * ((e / 4) * NT + tid) + (e % 4));
+    }
+    run += (uint32_t)__popcll(mask);
   }
-  auto taken = [&](int e) -> bool {
-    const uint64_t eqb = __ballot(key[e] == T);
-    const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)eq_base[e / kWave], e % kWave);
-    if (key[e] == T) return base + (uint32_t)__popcll(eqb & lt) < need;
-    return key[e] > T;
-  };
-  fence_keys(key);
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint64_t selb = __ballot(taken(e));
-    if (lane == 0) cnt_sel[e * NW + wid] = (uint32_t)__popcll(selb);
-  }
-  for (int i = E * NW + tid; i < kSlots; i += NT) cnt_sel[i] = 0u;
+  if (lane == 0) wcnt[wid] = run;
   __syncthreads();
-  scan_slots<NT>(cnt_sel, tmp);
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    const int e = v * kWave + lane;
-    sel_base[v] = e < E ? cnt_sel[e * NW + wid] : 0u;
+  uint32_t before = 0, total = 0;
+  bool over = false;
+  for (int w = 0; w < NW; ++w) {
+    if (w < wid) before += wcnt[w];
+    total += wcnt[w];
+    over |= wcnt[w] > (uint32_t)kCW;
   }
-  fence_keys(key);
+  if (!over) {
+    for (uint32_t i = lane; i < wcnt[wid]; i += kWave) {
+      cand_val[slot0 + before + i] = sval[wid * kCW + i];
+      cand_idx[slot0 + before + i] = sidx[wid * kCW + i];
+    }
+  }
+  if (tid == 0) cand_cnt[row * kMaxSlices + slice] = over ? kSliceCap + 1 : (int)total;
+}
+
+// ---------------------------------------------------------------------------
+// finish: one workgroup per row
+
+template <bool kFromCand, int MC>
+__global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
+    const float* __restrict__ scores, int gstride, const int32_t* __restrict__ row_len,
+    int first_pos, int max_ctx, int K, const uint32_t* __restrict__ cand_val,
+    const uint16_t* __restrict__ cand_idx, const int32_t* __restrict__ cand_cnt,
+    int32_t* __restrict__ out) {
+  constexpr int NT = kFinishThreads, NW = NT / kWave;
+  constexpr int kW = kMaxGroups / 32;
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
+  __shared__ uint32_t selmap[kW];
+  __shared__ uint32_t eqmap[kW];
+  __shared__ uint32_t tmp[2 * NW + 1];
+  __shared__ float red[2 * NW];
+  __shared__ int sh[4];
+
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int L = row_len ? row_len[row] : first_pos + row + 1;
+  int G = (L >= 0 && L <= max_ctx) ? L / kRatio : 0;
+  if (G > gstride) G = gstride;
+  int32_t* orow = out + (size_t)row * K;
+  if (G <= K) {  // every complete group is kept
+    for (int i = tid; i < K; i += NT) orow[i] = (i < G) ? i : -1;
+    return;
+  }
+  const float* srow = scores + (size_t)row * gstride;
+  const int nwords = (G + 31) / 32;
+  for (int i = tid; i < nwords; i += NT) { selmap[i] = 0u; eqmap[i] = 0u; }
+
+  // candidates: slot m*NT + tid
+  uint32_t ck[MC];
+  uint32_t cg[MC];
+  bool ok = true;
+  if (kFromCand) {
+    // slot m*NT + tid lies in slice m (kSliceCap == NT): every load below is
+    // independent, so all of them are in flight together
+    static_assert(kSliceCap == NT, "one slice per slot row");
+    const int n_slices = (G + kSlice - 1) / kSlice;
+    int cnt[MC];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const bool t = taken(e);
-    const uint64_t selb = __ballot(t);
-    if (t) {
-      const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)sel_base[e / kWave], e % kWave);
-      const uint32_t pos = base + (uint32_t)__popcll(selb & lt);
-      if (pos < (uint32_t)K) orow[pos] = e * NT + tid;
+    for (int m = 0; m < MC; ++m) cnt[m] = m < n_slices ? cand_cnt[row * kMaxSlices + m] : 0;
+    const size_t base = (size_t)row * kMaxSlices * kSliceCap;
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      ck[m] = cand_val[base + m * NT + tid];
+      cg[m] = cand_idx[base + m * NT + tid];
+    }
+    uint32_t C = 0;
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      ok &= cnt[m] <= kSliceCap;
+      C += (uint32_t)cnt[m];
+    }
+    ok &= C >= (uint32_t)K;
+#pragma unroll
+    for (int m = 0; m < MC; ++m)
+      ck[m] = (ok && tid < cnt[m]) ? score_key(__uint_as_float(ck[m])) : 0u;
+  } else {
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      const int i = m * NT + tid;
+      ck[m] = i < G ? score_key(srow[i]) : 0u;
+      cg[m] = (uint32_t)i;
+    }
+  }
+  uint32_t T, take_eq;
+  if (ok) {
+    T = candidate_threshold<NT, MC>(ck, (uint32_t)K, hist, tmp, sh, &take_eq);
+#pragma unroll
+    for (int m = 0; m < MC; ++m)
+      if (ck[m] >= T && ck[m]) atomicOr(ck[m] > T ? &selmap[cg[m] >> 5] : &eqmap[cg[m] >> 5],
+                                        1u << (cg[m] & 31));
+  } else {
+    // the pruning guess missed: exact ranking of the whole row
+    T = exact_threshold_stream<NT>(srow, G, (uint32_t)K, hist, red, sh, &take_eq);
+    for (int i = tid; i < G; i += NT) {
+      const uint32_t k = score_key(srow[i]);
+      if (k >= T) atomicOr(k > T ? &selmap[i >> 5] : &eqmap[i >> 5], 1u << (i & 31));
+    }
+  }
+  __syncthreads();
+
+  // bitmaps -> ascending indices; thread t owns words [2t, 2t + 2)
+  constexpr int WPT = kW / NT;
+  uint32_t sw[WPT], ew[WPT];
+  uint32_t n_eq = 0;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int w = tid * WPT + i;
+    sw[i] = w < nwords ? selmap[w] : 0u;
+    ew[i] = w < nwords ? eqmap[w] : 0u;
+    n_eq += (uint32_t)__popc(ew[i]);
+  }
+  uint32_t eq_before = block_excl_scan<NT>(n_eq, tmp);
+  uint32_t n_sel = 0;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    uint32_t w = ew[i];
+    while (w) {
+      const uint32_t bit = w & (~w + 1u);
+      if (eq_before < take_eq) sw[i] |= bit;
+      ++eq_before;
+      w ^= bit;
+    }
+    n_sel += (uint32_t)__popc(sw[i]);
+  }
+  uint32_t pos = block_excl_scan<NT>(n_sel, tmp);
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    uint32_t w = sw[i];
+    while (w) {
+      const int b = __ffs(w) - 1;
+      if (pos < (uint32_t)K) orow[pos] = 32 * (tid * WPT + i) + b;
+      ++pos;
+      w &= w - 1u;
     }
   }
 }
 
 }  // namespace
 
+size_t topk_workspace_bytes(int n_rows, int gstride) {
+  if (gstride <= kDirect) return 0;
+  const size_t slots = (size_t)n_rows * kMaxSlices * kSliceCap;
+  return slots * sizeof(uint32_t) + slots * sizeof(uint16_t) +
+         (size_t)n_rows * kMaxSlices * sizeof(int32_t) + 3 * 256;
+}
+
 hipError_t launch_topk(const float* scores, int gstride, int n_rows, const int32_t* row_len,
-                       int first_pos, int max_ctx, int K, int32_t* out, hipStream_t stream) {
+                       int first_pos, int max_ctx, int K, int32_t* out, void* ws,
+                       hipStream_t stream) {
   if (n_rows <= 0) return hipSuccess;
-  dim3 grid(n_rows);
-#define QSA_TOPK_CASE(NT, EV)                                                                   \
-  if (gstride <= (NT) * (EV)) {                                                                 \
-    hipLaunchKernelGGL((topk_kernel<NT, EV>), grid, dim3(NT), 0, stream, scores, gstride,      \
-                       row_len, first_pos, max_ctx, K, out);                                    \
-    return hipGetLastError();                                                                   \
+  if (gstride > kMaxGroups) return hipErrorInvalidValue;
+  if (gstride <= kDirect) {
+    hipLaunchKernelGGL((topk_finish_kernel<false, kDirect / kFinishThreads>), dim3(n_rows),
+                       dim3(kFinishThreads), 0, stream, scores, gstride, row_len, first_pos,
+                       max_ctx, K, nullptr, nullptr, nullptr, out);
+    return hipGetLastError();
   }
-  QSA_TOPK_CASE(256, 4)
-  QSA_TOPK_CASE(256, 16)
-  QSA_TOPK_CASE(512, 16)
-  QSA_TOPK_CASE(1024, 16)
-  QSA_TOPK_CASE(1024, 32)
-  QSA_TOPK_CASE(1024, 64)
-#undef QSA_TOPK_CASE
-  return hipErrorInvalidValue;
+  if (!ws) return hipErrorInvalidValue;
+  const size_t slots = (size_t)n_rows * kMaxSlices * kSliceCap;
+  char* p = reinterpret_cast<char*>(ws);
+  uint32_t* cval = reinterpret_cast<uint32_t*>(p);
+  p += (slots * sizeof(uint32_t) + 255) / 256 * 256;
+  uint16_t* cidx = reinterpret_cast<uint16_t*>(p);
+  p += (slots * sizeof(uint16_t) + 255) / 256 * 256;
+  int32_t* ccnt = reinterpret_cast<int32_t*>(p);
+  const int n_slices = (gstride + kSlice - 1) / kSlice;
+  hipLaunchKernelGGL(topk_extract_kernel, dim3(n_slices, n_rows), dim3(kExtractThreads), 0,
+                     stream, scores, gstride, row_len, first_pos, max_ctx, K, cval, cidx, ccnt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((topk_finish_kernel<true, kMaxSlices * kSliceCap / kFinishThreads>),
+                     dim3(n_rows), dim3(kFinishThreads), 0, stream, scores, gstride, row_len,
+                     first_pos, max_ctx, K, cval, cidx, ccnt, out);
+  return hipGetLastError();
 }
 
 }  // namespace qsa

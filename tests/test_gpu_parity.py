@@ -162,3 +162,42 @@ def test_index_topk_entry_point(gpu):
     G = (wl.row_len // 4).astype(np.int32)
     H.check_scores(sc.cpu().numpy(), ora_s, G, H.score_bound(wl))
     H.check_topk(grp.cpu().numpy(), sc.cpu().numpy(), oracle.topk(ora_s, G, 256), ora_s, G, 256)
+
+
+@pytest.mark.parametrize("K", [512, 2048])
+def test_decode_long_rows_pruned_topk(gpu, K):
+    # rows longer than 16,384 groups take the sample-pruned two-step top-K
+    lens = [262144, 4 * 17000 + 1, 100003, 70000]
+    wl = workload.decode_workload(600 + K, lens, kv_dtype="fp8", topk_groups=K)
+    _decode_check(wl, gpu)
+
+
+def test_decode_long_rows_all_tied(gpu):
+    # all scores +0: the pruning threshold keeps every group, the slices
+    # overflow and the exact full-row path must pick the lowest K indices
+    wl = workload.decode_workload(610, [262144, 200001], kv_dtype="fp8", topk_groups=2048)
+    wl.w_idx[:] = 0.0
+    _decode_check(wl, gpu)
+
+
+def test_decode_long_rows_sample_miss(gpu):
+    # the evenly spaced sample positions are made the top scorers, so the
+    # sample-derived threshold keeps fewer than K groups and the exact
+    # full-row path must take over
+    wl = workload.decode_workload(611, [262144], kv_dtype="fp8", topk_groups=2048)
+    G = 262144 // 4
+    gpp = 16
+    for i in range(512):
+        g = (i * G) // 512
+        page = wl.page_table[0, g // gpp]
+        wl.khat[page, g % gpp] = 4.0 * wl.q_idx[0]
+    _decode_check(wl, gpu)
+
+
+def test_decode_long_rows_coarse_scores(gpu):
+    # scores on a coarse grid: many exact ties at the K-th score
+    wl = workload.decode_workload(612, [262144, 150000], kv_dtype="bf16", topk_groups=2048)
+    wl.khat[:] = np.round(wl.khat)
+    wl.q_idx[:] = np.round(wl.q_idx)
+    wl.w_idx[:] = 0.5
+    _decode_check(wl, gpu)
