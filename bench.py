@@ -35,6 +35,15 @@ CONFIG_NAMES = {
 }
 
 
+# short names of the workloads, used for the profile summaries
+WORKLOAD_SLUG = {
+    1: "decode_b1_l8193_bf16_k512",
+    2: "decode_b8_l32k-64k_fp8_k512",
+    3: "decode_b8_l262144_fp8_k2048",
+    5: "mtp_b4x3_l131073_fp8_k1024",
+}
+
+
 def algorithmic_bytes(wl) -> dict:
     """Bytes a step must move at minimum: the k̂ of every complete group, the
     K/V rows of every selected token, indexer/attention queries, outputs
@@ -82,13 +91,91 @@ def measured_traffic(kernel: str, workload: str, digest: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
+COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read, 1 GiB written
+
+
+def calibrate_copy(dev) -> None:
+    """Three launches of a plain elementwise copy (negation) of known size, so
+    a counter run can scale FETCH_SIZE / WRITE_SIZE to bytes."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def _read_counters(path: str) -> dict:
+    """Mean counter value per kernel name from rocprofv3 counter_collection CSVs
+    found under ``path``."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    sums: dict = {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                key = (row["Kernel_Name"], row["Counter_Name"])
+                v = sums.setdefault(key, [0.0, 0])
+                v[0] += float(row["Counter_Value"])
+                v[1] += 1
+    return {k: v[0] / v[1] for k, v in sums.items()}
+
+
+def write_counters(fetch_dir: str, write_dir: str, workload_name: str, commands: list) -> None:
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch) into HBM bytes per launch, each scaled by what the counter reads
+    for the calibration copy; writes profiles/<kernel>__<workload>.counters.json
+    for the indexer kernel and a text table for every kernel."""
+    fetch, write = _read_counters(fetch_dir), _read_counters(write_dir)
+
+    def mean(d, sub, counter):
+        vals = [v for (k, c), v in d.items() if sub in k and c == counter]
+        return sum(vals) / len(vals) if vals else None
+
+    copy_f = mean(fetch, "neg_kernel", "FETCH_SIZE")
+    copy_w = mean(write, "neg_kernel", "WRITE_SIZE")
+    ff = COPY_BYTES / (copy_f * 1024.0)
+    fw = COPY_BYTES / (copy_w * 1024.0)
+    kernels = sorted({k for (k, c) in fetch} | {k for (k, c) in write})
+    lines = [f"# HBM traffic per dispatch (rocprofv3 FETCH_SIZE, WRITE_SIZE), workload {workload_name}", "",
+             "Commands:", *[f"    {c}" for c in commands], "",
+             f"Calibration copy (1 GiB in, 1 GiB out): FETCH_SIZE {copy_f:.0f} KiB -> factor "
+             f"{ff:.4f}; WRITE_SIZE {copy_w:.0f} KiB -> factor {fw:.4f}", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM bytes |",
+             "|---|---|---|---|"]
+    for k in kernels:
+        f_, w_ = mean(fetch, k, "FETCH_SIZE"), mean(write, k, "WRITE_SIZE")
+        if f_ is None or w_ is None:
+            continue
+        tot = f_ * 1024.0 * ff + w_ * 1024.0 * fw
+        lines.append(f"| {k[:90]} | {f_:.0f} | {w_:.0f} | {tot:.0f} |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"hbm_traffic__{workload_name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    sf = mean(fetch, "index_score_gemv_kernel", "FETCH_SIZE")
+    sw = mean(write, "index_score_gemv_kernel", "WRITE_SIZE")
+    rec = {"kernel": "index_score_gemv_kernel", "workload": workload_name,
+           "source_digest": source_digest("index_score.hip", "qsa_device.h"),
+           "fetch_kib": sf, "write_kib": sw, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
+           "fetch_factor": ff, "write_factor": fw,
+           "hbm_bytes_per_launch": sf * 1024.0 * ff + sw * 1024.0 * fw, "commands": commands}
+    with open(os.path.join(ROOT, "profiles",
+                           f"index_score_gemv__{workload_name}.counters.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
+def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
     """The oracle, unchanged, on this host: full decode steps of a bounded
     subset of requests, scaled to layer-steps/s of the whole batch."""
     import oracle
     reps, t_total, rows_done = 0, 0.0, 0
     b = 0
-    while t_total < budget_s and reps < 64:
+    while t_total < budget_s and reps < 4096:
         t0 = time.perf_counter()
         oracle.decode(wl, rows=[b])
         t_total += time.perf_counter() - t0
@@ -98,8 +185,9 @@ def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
     per_request = t_total / rows_done
     return {"value": 1.0 / (per_request * wl.batch), "unit": "layer-steps/s",
             "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{rows_done} of the {wl.batch} requests of one step, run one at a time "
-                      f"({t_total:.1f} s), scaled to the full batch"}
+            "sample": f"{rows_done} single-request decode passes (requests taken in turn from "
+                      f"the {wl.batch} of the workload; {t_total:.1f} s in all), the mean time "
+                      f"per request scaled to the full batch"}
 
 
 def main() -> int:
@@ -109,7 +197,16 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also launch a 1 GiB copy kernel (for counter runs)")
+    ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: summarise two rocprofv3 --pmc runs into profiles/")
+    ap.add_argument("--counter-commands", nargs="*", default=[],
+                    help="the commands that made the counter runs (recorded with them)")
     args = ap.parse_args()
+    if args.write_counters:
+        write_counters(*args.write_counters, WORKLOAD_SLUG[args.config], args.counter_commands)
+        return 0
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the QSA layer step is not sharded "
               "here); run with --gpus 1", file=sys.stderr)
@@ -169,7 +266,7 @@ def main() -> int:
     ab = algorithmic_bytes(wl)
     score_gbs = ab["score_kernel"] / (ms_score * 1e-3) / 1e9
     step_gbs = ab["step"] / (ms_step * 1e-3) / 1e9
-    wname = f"cfg{args.config}"
+    wname = WORKLOAD_SLUG[args.config]
     digest = source_digest("index_score.hip", "qsa_device.h")
     traffic = measured_traffic("index_score_gemv", wname, digest)
 
@@ -202,6 +299,8 @@ def main() -> int:
                           "frac": step_gbs / HBM_PEAK_GBS},
         "gen_seconds": round(t_gen, 1),
     }
+    if args.calibrate_copy:
+        calibrate_copy(dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result))

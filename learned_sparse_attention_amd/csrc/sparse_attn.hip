@@ -61,20 +61,31 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Rows handled: global query rows row_base .. row_base + 16*NB - 1 of the
-// item (row r = position r / gq, head r % gq of the KV head's group), of
-// which those < n_rows exist.
-template <bool kFp8, int NB>
+// Registers of one 16-token sub-tile in flight: lane l holds 64 contiguous
+// K bytes (fp8) / 128 bytes (bf16) of token lq = l % 16, and 16 / 32 bytes
+// of the V rows of tokens 4*lg + j (lg = l / 16).
+template <bool kFp8>
+struct SubTile {
+  u32x4 k[kFp8 ? 4 : 8];
+  u32x4 v[4][kFp8 ? 1 : 2];
+  int rv[4];  // physical rows of the four V tokens (-1: absent)
+};
+
+// One work item: the 16 query rows row_base .. row_base + 15 (row r =
+// position r / gq, head r % gq of the KV head's group; rows >= n_rows are
+// padding) over the item's token stream.
+template <bool kFp8>
 __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& it, int kvh,
                                             const uint16_t* q_rows, int q_row_stride,
                                             int row_base, int n_rows, int gq, float* acc_lds,
-                                            float* ml_lds, int32_t* tok_row, float* out_final,
-                                            float* out_partial) {
+                                            float* ml_lds, uint16_t* q_lds, int32_t* tok_row,
+                                            float* out_final, float* out_partial) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int lq = lane & 15, lg = lane >> 4;
   constexpr int kEsize = kFp8 ? 1 : 2;
   constexpr int kRowBytes = kHeadDim * kEsize;
+  constexpr int kQPitch = kHeadDim + 8;  // bf16 elements; spreads the 16 rows over LDS banks
 
   // ---- token stream -> physical row offsets (page * 64 + slot), -1 if absent
   const int n_groups = max(0, it.g_end - it.g_begin);
@@ -97,232 +108,224 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
     }
     tok_row[i] = r;
   }
+  // ---- the 16 query rows into LDS (zeros for padding rows)
+  for (int i = tid; i < 16 * (kHeadDim / 8); i += kAttnThreads) {
+    const int rl = i / (kHeadDim / 8), c = i % (kHeadDim / 8);
+    const int r = row_base + rl;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < n_rows)
+      v = *reinterpret_cast<const u32x4*>(q_rows + (size_t)(r / gq) * q_row_stride +
+                                          (size_t)(r % gq) * kHeadDim + 8 * c);
+    *reinterpret_cast<u32x4*>(q_lds + rl * kQPitch + 8 * c) = v;
+  }
   __syncthreads();
 
-  // ---- query operands: lane supplies Q[row 16*nb + lq][64*lg + 8*ks + 0..7]
-  bf16x8 qop[NB][8];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int r = row_base + nb * 16 + lq;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (r < n_rows) {
-        const uint16_t* qp = q_rows + (size_t)(r / gq) * q_row_stride + (size_t)(r % gq) * kHeadDim;
-        v = *reinterpret_cast<const u32x4*>(qp + 64 * lg + 8 * ks);
-      }
-      qop[nb][ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-  // causal limit of this lane's query rows (only extra tokens can exceed it)
-  int limit[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) limit[nb] = it.base_len + (row_base + nb * 16 + lq) / gq;
-
+  // causal limit of this lane's query row (only extra tokens can exceed it)
+  const int limit = it.base_len + (row_base + lq) / gq;
   const float qk_scale = a.sm_scale * a.k_scale * kLog2e;
-  float m_run[NB], l_run[NB];
-  float4_t acc[NB][16];
+  float m_run = -INFINITY, l_run = 0.0f;
+  float4_t acc[16];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    m_run[nb] = -INFINITY;
-    l_run[nb] = 0.0f;
-#pragma unroll
-    for (int mb = 0; mb < 16; ++mb) acc[nb][mb] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  }
+  for (int mb = 0; mb < 16; ++mb) acc[mb] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
   const uint8_t* kc = reinterpret_cast<const uint8_t*>(a.k);
   const uint8_t* vc = reinterpret_cast<const uint8_t*>(a.v);
   const int Hkv = a.Hkv;
 
-  for (int s = wave; s < n_sub; s += kAttnWaves) {
-    // K: token 16s + lq, bytes [64*lg*esize, +64*esize) of its row
+  // K rows are fetched in four 16-byte pieces by separate instructions, so
+  // they are cached normally (the pieces meet in L2); each lane's V piece is
+  // read once, whole, and streamed past the caches.
+  auto load = [&](SubTile<kFp8>& b, int s) {
     const int rk = tok_row[16 * s + lq];
     const uint8_t* kp = kc + ((size_t)max(rk, 0) * Hkv + kvh) * kRowBytes + 64 * lg * kEsize;
-    u32x4 kraw[kFp8 ? 4 : 8];
 #pragma unroll
-    for (int i = 0; i < (kFp8 ? 4 : 8); ++i) kraw[i] = reinterpret_cast<const u32x4*>(kp)[i];
-    // V: tokens 16s + 4*lg + j, bytes [16*lq*esize, +16*esize)
-    int rv[4];
-    u32x4 vraw[4][kFp8 ? 1 : 2];
+    for (int i = 0; i < (kFp8 ? 4 : 8); ++i) b.k[i] = *reinterpret_cast<const u32x4*>(kp + 16 * i);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      rv[j] = tok_row[16 * s + 4 * lg + j];
-      const uint8_t* vp = vc + ((size_t)max(rv[j], 0) * Hkv + kvh) * kRowBytes + 16 * lq * kEsize;
+      b.rv[j] = tok_row[16 * s + 4 * lg + j];
+      const uint8_t* vp = vc + ((size_t)max(b.rv[j], 0) * Hkv + kvh) * kRowBytes + 16 * lq * kEsize;
 #pragma unroll
-      for (int i = 0; i < (kFp8 ? 1 : 2); ++i) vraw[j][i] = reinterpret_cast<const u32x4*>(vp)[i];
+      for (int i = 0; i < (kFp8 ? 1 : 2); ++i) b.v[j][i] = stream_load_u4(vp + 16 * i);
     }
+  };
 
-    // S^T = K . Q^T
-    float4_t sc[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) sc[nb] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const SubTile<kFp8>& b, int s) {
+    // S^T = K . Q^T (Q operand from LDS: row lq, d = 64*lg + 8*ks + 0..7)
+    float4_t sc = (float4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       bf16x8 kop;
       if (kFp8) {
-        const u32x4 w = kraw[ks / 2];
+        const u32x4 w = b.k[ks / 2];
         kop = (ks & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
       } else {
-        kop = __builtin_bit_cast(bf16x8, kraw[ks]);
+        kop = __builtin_bit_cast(bf16x8, b.k[ks]);
       }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[nb][ks], sc[nb], 0, 0, 0);
+      const bf16x8 qop = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(q_lds + lq * kQPitch + 64 * lg + 8 * ks));
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop, sc, 0, 0, 0);
     }
-
     // token of D row 4*lg + i is stream entry 16s + 4*lg + i (= V token i)
-    bool tok_ok[4];
-    int tok_id[4];
+    float sv[4];
+    float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int si = 16 * s + 4 * lg + i;
-      tok_ok[i] = rv[i] >= 0;
-      tok_id[i] = si < 4 * n_groups ? -1 : it.x_begin + (si - 4 * n_groups);  // -1: always visible
+      const int tok = si < 4 * n_groups ? -1 : it.x_begin + (si - 4 * n_groups);  // -1: visible
+      const bool vis = b.rv[i] >= 0 && tok < limit;
+      sv[i] = vis ? sc[i] * qk_scale : -INFINITY;
+      tmax = fmaxf(tmax, sv[i]);
     }
-
-    // online softmax, one query row per lane (replicated over the 4 lane
-    // groups).  The weights enter the PV product as a bf16 pair hi + lo
-    // (hi = bf16(p), lo = bf16(p - hi)), i.e. with ~16 significant bits, so
-    // the bf16 operand rounding does not show in outputs of few tokens.
-    short4_t pb_hi[NB], pb_lo[NB];
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    // Lazy running max: the accumulators (held in AGPRs) are rescaled only
+    // when a row's max grows by more than 2^8, so weights stay <= 256.
+    const bool grow = tmax > m_run + 8.0f;
+    if (__any(grow)) {
+      const float m_new = grow ? tmax : m_run;
+      const float alpha = (m_run == -INFINITY || m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float sv[4];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool vis = tok_ok[i] && (tok_id[i] < limit[nb]);
-        sv[i] = vis ? sc[nb][i] * qk_scale : -INFINITY;
-        tmax = fmaxf(tmax, sv[i]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      const float m_new = fmaxf(m_run[nb], tmax);
-      const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run[nb] - m_new);
-      float psum = 0.0f;
-      uint32_t hb[4], lb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = (m_new == -INFINITY) ? 0.0f : exp2f(sv[i] - m_new);
-        hb[i] = bf16_rne_bits(p);
-        lb[i] = bf16_rne_bits(p - __uint_as_float(hb[i] << 16));
-        psum += p;
-      }
-      l_run[nb] = l_run[nb] * alpha + psum;
-      m_run[nb] = m_new;
-#pragma unroll
-      for (int mb = 0; mb < 16; ++mb) acc[nb][mb] *= alpha;
-      pb_hi[nb] = (short4_t){(short)hb[0], (short)hb[1], (short)hb[2], (short)hb[3]};
-      pb_lo[nb] = (short4_t){(short)lb[0], (short)lb[1], (short)lb[2], (short)lb[3]};
+      for (int mb = 0; mb < 16; ++mb) acc[mb] *= alpha;
+      m_run = m_new;
     }
-
+    // weights as a bf16 hi + lo pair (~16 significant bits) for the PV MFMA
+    float psum = 0.0f;
+    uint32_t hb[4], lb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = (m_run == -INFINITY) ? 0.0f : exp2f(sv[i] - m_run);
+      hb[i] = bf16_rne_bits(p);
+      lb[i] = bf16_rne_bits(p - __uint_as_float(hb[i] << 16));
+      psum += p;
+    }
+    l_run += psum;
+    const short4_t p_hi = (short4_t){(short)hb[0], (short)hb[1], (short)hb[2], (short)hb[3]};
+    const short4_t p_lo = (short4_t){(short)lb[0], (short)lb[1], (short)lb[2], (short)lb[3]};
     // O^T += V^T . P^T; m-block mb holds d = 64*lg' + 16*i + mb for D row 4*lg' + i
-    uint32_t cv[4][8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (kFp8) {
-        const u32x4 w = tok_ok[j] ? vraw[j][0] : (u32x4){0u, 0u, 0u, 0u};
-        cv[j][0] = fp8x2_to_bf16x2<false>(w.x); cv[j][1] = fp8x2_to_bf16x2<true>(w.x);
-        cv[j][2] = fp8x2_to_bf16x2<false>(w.y); cv[j][3] = fp8x2_to_bf16x2<true>(w.y);
-        cv[j][4] = fp8x2_to_bf16x2<false>(w.z); cv[j][5] = fp8x2_to_bf16x2<true>(w.z);
-        cv[j][6] = fp8x2_to_bf16x2<false>(w.w); cv[j][7] = fp8x2_to_bf16x2<true>(w.w);
-      } else {
-        const u32x4 w0 = tok_ok[j] ? vraw[j][0] : (u32x4){0u, 0u, 0u, 0u};
-        const u32x4 w1 = tok_ok[j] ? vraw[j][1] : (u32x4){0u, 0u, 0u, 0u};
-        cv[j][0] = w0.x; cv[j][1] = w0.y; cv[j][2] = w0.z; cv[j][3] = w0.w;
-        cv[j][4] = w1.x; cv[j][5] = w1.y; cv[j][6] = w1.z; cv[j][7] = w1.w;
+    for (int qd = 0; qd < 8; ++qd) {
+      uint32_t cv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (kFp8) {
+          const u32x4 w = b.rv[j] >= 0 ? b.v[j][0] : (u32x4){0u, 0u, 0u, 0u};
+          const uint32_t word = qd < 2 ? w.x : qd < 4 ? w.y : qd < 6 ? w.z : w.w;
+          cv[j] = (qd & 1) ? fp8x2_to_bf16x2<true>(word) : fp8x2_to_bf16x2<false>(word);
+        } else {
+          const u32x4 w = b.rv[j] >= 0 ? b.v[j][qd / 4] : (u32x4){0u, 0u, 0u, 0u};
+          const int e = qd % 4;
+          cv[j] = e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int mb = 2 * qd + h;
+        const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+        const uint32_t lo = __builtin_amdgcn_perm(cv[1], cv[0], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(cv[3], cv[2], sel);
+        const short4_t vop = __builtin_bit_cast(short4_t, (u32x2){lo, hi});
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, p_hi, acc[mb], 0, 0, 0);
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, p_lo, acc[mb], 0, 0, 0);
       }
     }
+  };
+
+  // ---- main loop: rounds of kNS sub-tiles per wave (sub-tiles
+  // wave + 4*i); a round issues all of its loads before computing any of
+  // them, so one memory latency covers kNS sub-tiles
+  constexpr int kNS = 2;
+  for (int s0 = wave; s0 < n_sub; s0 += kNS * kAttnWaves) {
+    SubTile<kFp8> bt[kNS];
 #pragma unroll
-    for (int mb = 0; mb < 16; ++mb) {
-      const int qd = mb >> 1;
-      const uint32_t sel = (mb & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t lo = __builtin_amdgcn_perm(cv[1][qd], cv[0][qd], sel);
-      const uint32_t hi = __builtin_amdgcn_perm(cv[3][qd], cv[2][qd], sel);
-      const short4_t vop = __builtin_bit_cast(short4_t, (u32x2){lo, hi});
+    for (int i = 0; i < kNS; ++i)
+      if (s0 + i * kAttnWaves < n_sub) load(bt[i], s0 + i * kAttnWaves);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pb_hi[nb], acc[nb][mb], 0, 0, 0);
-        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pb_lo[nb], acc[nb][mb], 0, 0, 0);
-      }
-    }
+    for (int i = 0; i < kNS; ++i)
+      if (s0 + i * kAttnWaves < n_sub) compute(bt[i], s0 + i * kAttnWaves);
   }
 
-  // ---- merge the 4 waves: row maxima and sums, then accumulators in order
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    float l = l_run[nb];
+  // ---- merge the 4 waves.  Each wave publishes its row maxima and sums,
+  // then writes its accumulators, rescaled to the row's common max, into
+  // its own LDS slice; the block sums the slices while writing out.
+  {
+    float l = l_run;
     l += __shfl_xor(l, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
     if (lg == 0) {
-      ml_lds[(wave * NB + nb) * 32 + lq] = m_run[nb];
-      ml_lds[(wave * NB + nb) * 32 + 16 + lq] = l;
+      ml_lds[wave * 32 + lq] = m_run;
+      ml_lds[wave * 32 + 16 + lq] = l;
     }
   }
   __syncthreads();
-  float fac[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+  const int rows_here = min(16, n_rows - row_base);
+  {
     float M = -INFINITY;
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, ml_lds[(w * NB + nb) * 32 + lq]);
-    fac[nb] = (M == -INFINITY) ? 0.0f : exp2f(m_run[nb] - M);
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, ml_lds[w * 32 + lq]);
+    const float fac = (M == -INFINITY || m_run == -INFINITY) ? 0.0f : exp2f(m_run - M);
+    if (lq < rows_here) {
+      float* rowp = acc_lds + ((size_t)wave * 16 + lq) * kAccPitch;
+#pragma unroll
+      for (int mb = 0; mb < 16; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rowp[64 * lg + 16 * i + mb] = acc[mb][i] * fac;
+    }
   }
-  for (int w = 0; w < kAttnWaves; ++w) {
-    if (wave == w) {
+  // row statistics: common max and the sum of the rescaled row sums
+  if (tid < 16) {
+    float M = -INFINITY;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        float* rowp = acc_lds + (size_t)(nb * 16 + lq) * kAccPitch;
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, ml_lds[w * 32 + tid]);
+    float Lsum = 0.0f;
+    if (M != -INFINITY) {
 #pragma unroll
-        for (int mb = 0; mb < 16; ++mb) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int d = 64 * lg + 16 * i + mb;
-            const float v = acc[nb][mb][i] * fac[nb];
-            rowp[d] = (w == 0) ? v : rowp[d] + v;
-          }
-        }
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float mw = ml_lds[w * 32 + tid];
+        if (mw != -INFINITY) Lsum += exp2f(mw - M) * ml_lds[w * 32 + 16 + tid];
       }
     }
-    __syncthreads();
+    ml_lds[kAttnWaves * 32 + tid] = M;
+    ml_lds[kAttnWaves * 32 + 16 + tid] = Lsum;
   }
+  __syncthreads();
 
   // ---- write: normalised rows, or (max, sum, accumulator) partials
-  for (int r = 0; r < min(16 * NB, n_rows - row_base); ++r) {
-    const int nb = r / 16, rl = r % 16;
-    float M = -INFINITY, Lsum = 0.0f;
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, ml_lds[(w * NB + nb) * 32 + rl]);
-    if (M != -INFINITY)
-      for (int w = 0; w < kAttnWaves; ++w) {
-        const float mw = ml_lds[(w * NB + nb) * 32 + rl];
-        if (mw != -INFINITY) Lsum += exp2f(mw - M) * ml_lds[(w * NB + nb) * 32 + 16 + rl];
-      }
-    const float* rowp = acc_lds + (size_t)r * kAccPitch;
-    for (int d = tid; d < kHeadDim; d += kAttnThreads) {
-      const int rg = row_base + r;
-      if (out_final) {
-        const float o = (Lsum > 0.0f) ? rowp[d] * (a.v_scale / Lsum) : 0.0f;
-        out_final[(size_t)(rg / gq) * ((size_t)a.Hq * kHeadDim) + (size_t)(rg % gq) * kHeadDim + d] = o;
-      } else {
-        float* pp = out_partial + (size_t)rg * (2 + kHeadDim);
-        if (d == 0) { pp[0] = M; pp[1] = Lsum; }
-        pp[2 + d] = rowp[d];
-      }
+  for (int e = tid; e < rows_here * kHeadDim; e += kAttnThreads) {
+    const int r = e / kHeadDim, d = e % kHeadDim;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) v += acc_lds[((size_t)w * 16 + r) * kAccPitch + d];
+    const int rg = row_base + r;
+    if (out_final) {
+      const float Lsum = ml_lds[kAttnWaves * 32 + 16 + r];
+      out_final[(size_t)(rg / gq) * ((size_t)a.Hq * kHeadDim) + (size_t)(rg % gq) * kHeadDim + d] =
+          Lsum > 0.0f ? v * (a.v_scale / Lsum) : 0.0f;
+    } else {
+      out_partial[(size_t)rg * (2 + kHeadDim) + 2 + d] = v;
     }
+  }
+  if (!out_final && tid < rows_here) {
+    out_partial[(size_t)(row_base + tid) * (2 + kHeadDim)] = ml_lds[kAttnWaves * 32 + tid];
+    out_partial[(size_t)(row_base + tid) * (2 + kHeadDim) + 1] = ml_lds[kAttnWaves * 32 + 16 + tid];
   }
 }
 
-template <bool kFp8, int NB>
-__global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnArgs a) {
+constexpr int kQLdsElems = 16 * (kHeadDim + 8);
+
+template <bool kFp8>
+__global__ __launch_bounds__(kAttnThreads, kFp8 ? 2 : 1) void attn_decode_kernel(AttnArgs a) {
   extern __shared__ float smem[];
   const int gq = a.Hq / a.Hkv;
   const int Q = a.q_per_req;
   const int n_rows = Q * gq;
-  const int nblk = (n_rows + 16 * NB - 1) / (16 * NB);
+  const int nblk = (n_rows + 15) / 16;
   const int split = blockIdx.x / nblk, rb = blockIdx.x % nblk;
   const int kvh = blockIdx.y, b = blockIdx.z;
   float* acc_lds = smem;
-  float* ml_lds = acc_lds + NB * 16 * kAccPitch;
-  int32_t* tok_row = reinterpret_cast<int32_t*>(ml_lds + kAttnWaves * NB * 32);
+  float* ml_lds = acc_lds + kAttnWaves * 16 * kAccPitch;
+  uint16_t* q_lds = reinterpret_cast<uint16_t*>(ml_lds + (kAttnWaves + 1) * 32);
+  int32_t* tok_row = reinterpret_cast<int32_t*>(q_lds + kQLdsElems);
 
   const int L0 = a.ctx_lens[b];
   const bool valid = L0 >= 0 && L0 <= a.max_ctx - (Q - 1);
@@ -340,18 +343,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnArgs a) {
 
   const uint16_t* q_rows = a.q + ((size_t)b * Q * a.Hq + (size_t)kvh * gq) * kHeadDim;
   float* part = a.partial + (((size_t)b * a.Hkv + kvh) * a.n_splits + split) * n_rows * (2 + kHeadDim);
-  attend_item<kFp8, NB>(a, it, kvh, q_rows, a.Hq * kHeadDim, rb * 16 * NB, n_rows, gq, acc_lds,
-                        ml_lds, tok_row, nullptr, part);
+  attend_item<kFp8>(a, it, kvh, q_rows, a.Hq * kHeadDim, rb * 16, n_rows, gq, acc_lds, ml_lds,
+                    q_lds, tok_row, nullptr, part);
 }
 
-template <bool kFp8, int NB>
-__global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(AttnArgs a) {
+template <bool kFp8>
+__global__ __launch_bounds__(kAttnThreads, kFp8 ? 2 : 1) void attn_prefill_kernel(AttnArgs a) {
   extern __shared__ float smem[];
   const int qi = blockIdx.x, kvh = blockIdx.y;
   const int gq = a.Hq / a.Hkv;
   float* acc_lds = smem;
-  float* ml_lds = acc_lds + NB * 16 * kAccPitch;
-  int32_t* tok_row = reinterpret_cast<int32_t*>(ml_lds + kAttnWaves * NB * 32);
+  float* ml_lds = acc_lds + kAttnWaves * 16 * kAccPitch;
+  uint16_t* q_lds = reinterpret_cast<uint16_t*>(ml_lds + (kAttnWaves + 1) * 32);
+  int32_t* tok_row = reinterpret_cast<int32_t*>(q_lds + kQLdsElems);
 
   const int L = a.first_pos + qi + 1;
   const int G = L / kRatio;
@@ -365,7 +369,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(AttnArgs a) 
   it.base_len = L;
   const uint16_t* q_rows = a.q + ((size_t)qi * a.Hq + (size_t)kvh * gq) * kHeadDim;
   float* outp = a.out + ((size_t)qi * a.Hq + (size_t)kvh * gq) * kHeadDim;
-  attend_item<kFp8, NB>(a, it, kvh, q_rows, 0, 0, gq, gq, acc_lds, ml_lds, tok_row, outp, nullptr);
+  attend_item<kFp8>(a, it, kvh, q_rows, 0, 0, gq, gq, acc_lds, ml_lds, q_lds, tok_row, outp,
+                    nullptr);
 }
 
 // Merge split partials: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
@@ -423,20 +428,20 @@ __global__ void expand_tokens_kernel(const int32_t* __restrict__ sel, int K,
   }
 }
 
-size_t attn_smem_bytes(int NB, int stream_cap) {
-  return sizeof(float) * ((size_t)NB * 16 * kAccPitch + (size_t)kAttnWaves * NB * 32) +
-         sizeof(int32_t) * (size_t)((stream_cap + 15) / 16 * 16);
+size_t attn_smem_bytes(int stream_cap) {
+  return sizeof(float) * ((size_t)kAttnWaves * 16 * kAccPitch + (size_t)(kAttnWaves + 1) * 32) +
+         sizeof(uint16_t) * (size_t)kQLdsElems + sizeof(int32_t) * (size_t)((stream_cap + 15) / 16 * 16);
 }
 
-template <bool kFp8, int NB>
-hipError_t launch_decode_nb(const AttnArgs& a, hipStream_t stream) {
+template <bool kFp8>
+hipError_t launch_decode_t(const AttnArgs& a, hipStream_t stream) {
   if (a.n_splits > kMaxSplits) return hipErrorInvalidValue;
   const int cap = 4 * a.groups_per_split + 3 + (a.q_per_req - 1);
-  const size_t smem = attn_smem_bytes(NB, cap);
+  const size_t smem = attn_smem_bytes(cap);
   const int rows = a.q_per_req * (a.Hq / a.Hkv);
-  const int nblk = (rows + 16 * NB - 1) / (16 * NB);
+  const int nblk = (rows + 15) / 16;
   dim3 grid(a.n_splits * nblk, a.Hkv, a.batch);
-  hipLaunchKernelGGL((attn_decode_kernel<kFp8, NB>), grid, dim3(kAttnThreads), smem, stream, a);
+  hipLaunchKernelGGL((attn_decode_kernel<kFp8>), grid, dim3(kAttnThreads), smem, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 cgrid(a.Hq, a.q_per_req, a.batch);
@@ -445,28 +450,22 @@ hipError_t launch_decode_nb(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool kFp8, int NB>
-hipError_t launch_prefill_nb(const AttnArgs& a, hipStream_t stream) {
-  const int cap = 4 * a.K + 3;
-  const size_t smem = attn_smem_bytes(NB, cap);
+template <bool kFp8>
+hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
+  if (a.Hq / a.Hkv > 16) return hipErrorInvalidValue;
+  const size_t smem = attn_smem_bytes(4 * a.K + 3);
   dim3 grid(a.batch, a.Hkv);
-  hipLaunchKernelGGL((attn_prefill_kernel<kFp8, NB>), grid, dim3(kAttnThreads), smem, stream, a);
+  hipLaunchKernelGGL((attn_prefill_kernel<kFp8>), grid, dim3(kAttnThreads), smem, stream, a);
   return hipGetLastError();
-}
-
-template <int NB>
-hipError_t dispatch_dtype(const AttnArgs& a, hipStream_t stream, bool prefill) {
-  if (a.kv_dtype == 1)
-    return prefill ? launch_prefill_nb<true, NB>(a, stream) : launch_decode_nb<true, NB>(a, stream);
-  return prefill ? launch_prefill_nb<false, NB>(a, stream) : launch_decode_nb<false, NB>(a, stream);
 }
 
 // One 16-row block per workgroup: query rows beyond 16 (e.g. 12 heads x 3
 // draft positions) take further workgroups over the same tokens, which
 // then mostly come from the caches.
 hipError_t dispatch(const AttnArgs& a, hipStream_t stream, bool prefill) {
-  if (prefill && a.Hq / a.Hkv > 16) return hipErrorInvalidValue;
-  return dispatch_dtype<1>(a, stream, prefill);
+  if (a.kv_dtype == 1)
+    return prefill ? launch_prefill_t<true>(a, stream) : launch_decode_t<true>(a, stream);
+  return prefill ? launch_prefill_t<false>(a, stream) : launch_decode_t<false>(a, stream);
 }
 
 }  // namespace
