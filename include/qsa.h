@@ -154,6 +154,23 @@ qsa_status qsa_index_score(const qsa_geometry* g, const qsa_paged_cache* cache,
                            const int32_t* row_len, const float* q_idx,
                            const float* w_idx, float* out_scores, void* stream);
 
+/* Indexer scores of a prefill chunk (step 1 for every query of the chunk),
+ * exactly as qsa_prefill computes them: a dense GEMM on the matrix cores
+ * with q_idx and k̂ rounded to bf16 (round-to-nearest-even), exact
+ * products, fp32 sums; w_idx, the ReLU and the head sum stay fp32.  No
+ * workspace.
+ *
+ *   req, first_pos, n_q, q_idx, w_idx: as for qsa_prefill (query i has
+ *             L = first_pos + i + 1).
+ *   out_scores [n_q, (first_pos + n_q) / ratio] f32; entries
+ *             g >= floor(L_i / 4) are -inf, and so are groups on
+ *             out-of-range pages.
+ */
+qsa_status qsa_index_score_prefill(const qsa_geometry* g, const qsa_paged_cache* cache,
+                                   int32_t req, int32_t first_pos, int32_t n_q,
+                                   const float* q_idx, const float* w_idx,
+                                   float* out_scores, void* stream);
+
 /* Indexer score + exact top-K for independent query rows (steps 1-2 above),
  * fp32 arithmetic (a GEMV per row over the paged k̂).
  *

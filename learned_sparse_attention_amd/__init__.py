@@ -18,8 +18,8 @@ import math
 import os
 
 __all__ = ["QSAError", "load", "validate", "token_width", "index_topk_workspace_size",
-           "decode_workspace_size", "prefill_workspace_size", "qsa_index_score", "qsa_index_topk", "qsa_decode",
-           "qsa_prefill", "LIB_PATH"]
+           "decode_workspace_size", "prefill_workspace_size", "qsa_index_score",
+           "qsa_index_score_prefill", "qsa_index_topk", "qsa_decode", "qsa_prefill", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsa.so")
 
@@ -76,6 +76,8 @@ def load():
             f.argtypes = args
         L.qsa_index_score.restype = ctypes.c_int
         L.qsa_index_score.argtypes = [G, C, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.qsa_index_score_prefill.restype = ctypes.c_int
+        L.qsa_index_score_prefill.argtypes = [G, C, i32, i32, i32, vp, vp, vp, vp]
         L.qsa_index_topk.restype = ctypes.c_int
         L.qsa_index_topk.argtypes = [G, C, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.qsa_decode.restype = ctypes.c_int
@@ -168,6 +170,25 @@ def qsa_index_score(geom, khat, page_table, row_req, row_len, q_idx, w_idx, max_
     code = load().qsa_index_score(ctypes.byref(g), ctypes.byref(c), n, int(max_ctx),
                                   *(_ptr(t) for t in args), _ptr(out_scores), _stream(dev))
     _check("qsa_index_score", code)
+    return out_scores
+
+
+def qsa_index_score_prefill(geom, khat, page_table, req, first_pos, q_idx, w_idx,
+                            out_scores=None, num_pages=None):
+    """Indexer scores of a prefill chunk on the matrix cores (bf16 operands,
+    fp32 sums).  Query i has L = first_pos + i + 1.  Returns out_scores
+    [n_q, (first_pos + n_q) // 4]."""
+    import torch
+    dev = q_idx.device
+    n = int(q_idx.shape[0])
+    if out_scores is None:
+        out_scores = torch.empty((n, (first_pos + n) // 4), dtype=torch.float32, device=dev)
+    g = _geom(geom)
+    c, keep = _cache(None, None, khat, page_table, num_pages)
+    code = load().qsa_index_score_prefill(ctypes.byref(g), ctypes.byref(c), int(req),
+                                          int(first_pos), n, _ptr(_c(q_idx)), _ptr(_c(w_idx)),
+                                          _ptr(out_scores), _stream(dev))
+    _check("qsa_index_score_prefill", code)
     return out_scores
 
 

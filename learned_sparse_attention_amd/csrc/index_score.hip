@@ -32,11 +32,6 @@ __device__ __forceinline__ float dot4(float4 a, float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
 
-__device__ __forceinline__ float4 round4(float4 a) {
-  return make_float4(bf16_round(a.x), bf16_round(a.y), bf16_round(a.z), bf16_round(a.w));
-}
-
-template <bool kRound>
 __global__ __launch_bounds__(kScoreThreads) void index_score_gemv_kernel(
     const float* __restrict__ khat, const int32_t* __restrict__ page_table, int max_pages,
     int num_pages, const int32_t* __restrict__ row_req, const int32_t* __restrict__ row_len,
@@ -56,7 +51,6 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_gemv_kernel(
   const float* qrow = q_idx + (size_t)row * kGroupFloats;
   float4 qa = *reinterpret_cast<const float4*>(qrow + hA * kIdxDim + d0);
   float4 qb = *reinterpret_cast<const float4*>(qrow + hB * kIdxDim + d0);
-  if (kRound) { qa = round4(qa); qb = round4(qb); }
   const float wa = w_idx[(size_t)row * kIdxHeads + hA];
   const float wb = w_idx[(size_t)row * kIdxHeads + hB];
 
@@ -79,7 +73,6 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_gemv_kernel(
         for (int g = 0; g < kGroupsPerPage; ++g) {
           float4 x0 = stream_load(base + g * 128 + lane);
           float4 x1 = stream_load(base + g * 128 + 64 + lane);
-          if (kRound) { x0 = round4(x0); x1 = round4(x1); }
           float p0 = row16_sum(dot4(x0, qa));
           float p1 = row16_sum(dot4(x1, qb));
           v[g] = wa * fmaxf(p0, 0.0f) + wb * fmaxf(p1, 0.0f);
@@ -103,18 +96,13 @@ hipError_t launch_index_score_gemv(const float* khat, const int32_t* page_table,
                                    int num_pages, int n_rows, const int32_t* row_req,
                                    const int32_t* row_len, int req0, int first_pos, int max_ctx,
                                    const float* q_idx, const float* w_idx, float* scores,
-                                   int gstride, bool round_bf16, hipStream_t stream) {
+                                   int gstride, hipStream_t stream) {
   if (n_rows <= 0 || gstride <= 0) return hipSuccess;
   const int row_pages = (gstride + kGroupsPerPage - 1) / kGroupsPerPage;
   dim3 grid((row_pages + kPagesPerBlock - 1) / kPagesPerBlock, n_rows, 1);
-  if (round_bf16)
-    hipLaunchKernelGGL(index_score_gemv_kernel<true>, grid, dim3(kScoreThreads), 0, stream, khat,
-                       page_table, max_pages, num_pages, row_req, row_len, req0, first_pos, max_ctx,
-                       q_idx, w_idx, scores, gstride);
-  else
-    hipLaunchKernelGGL(index_score_gemv_kernel<false>, grid, dim3(kScoreThreads), 0, stream, khat,
-                       page_table, max_pages, num_pages, row_req, row_len, req0, first_pos, max_ctx,
-                       q_idx, w_idx, scores, gstride);
+  hipLaunchKernelGGL(index_score_gemv_kernel, grid, dim3(kScoreThreads), 0, stream, khat,
+                     page_table, max_pages, num_pages, row_req, row_len, req0, first_pos, max_ctx,
+                     q_idx, w_idx, scores, gstride);
   return hipGetLastError();
 }
 

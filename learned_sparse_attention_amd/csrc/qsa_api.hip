@@ -185,8 +185,24 @@ qsa_status qsa_index_score(const qsa_geometry* g, const qsa_paged_cache* cache, 
   if (!row_len || !q_idx || !w_idx || !out_scores) return QSA_ERR_INVALID_ARG;
   QSA_HIP(launch_index_score_gemv(cache->khat, cache->page_table, cache->max_pages,
                                   cache->num_pages, n_rows, row_req, row_len, 0, 0, max_ctx,
-                                  q_idx, w_idx, out_scores, gstride_of(max_ctx), false,
+                                  q_idx, w_idx, out_scores, gstride_of(max_ctx),
                                   (hipStream_t)stream));
+  return QSA_OK;
+}
+
+qsa_status qsa_index_score_prefill(const qsa_geometry* g, const qsa_paged_cache* cache,
+                                   int32_t req, int32_t first_pos, int32_t n_q, const float* q_idx,
+                                   const float* w_idx, float* out_scores, void* stream) {
+  qsa_status st = qsa_validate(g);
+  if (st != QSA_OK) return st;
+  if (req < 0 || first_pos < 0 || n_q < 0 || !cache_ok(cache, false)) return QSA_ERR_INVALID_ARG;
+  const long long total = (long long)first_pos + n_q;
+  if (total > kCapacity || total > (long long)cache->max_pages * kPage) return QSA_ERR_INVALID_ARG;
+  if (n_q == 0) return QSA_OK;
+  if (!q_idx || !w_idx || !out_scores) return QSA_ERR_INVALID_ARG;
+  QSA_HIP(launch_index_score_prefill(cache->khat, cache->page_table, cache->max_pages,
+                                     cache->num_pages, req, first_pos, n_q, q_idx, w_idx,
+                                     out_scores, gstride_of((int)total), (hipStream_t)stream));
   return QSA_OK;
 }
 
@@ -207,7 +223,7 @@ qsa_status qsa_index_topk(const qsa_geometry* g, const qsa_paged_cache* cache, i
   float* scores = out_scores ? out_scores : (float*)((char*)ws + lay.off_scores);
   QSA_HIP(launch_index_score_gemv(cache->khat, cache->page_table, cache->max_pages,
                                   cache->num_pages, n_rows, row_req, row_len, 0, 0, max_ctx,
-                                  q_idx, w_idx, scores, lay.gstride, false, s));
+                                  q_idx, w_idx, scores, lay.gstride, s));
   QSA_HIP(launch_topk(scores, lay.gstride, n_rows, row_len, 0, max_ctx, g->topk_groups,
                       out_groups, (char*)ws + lay.off_topk, s));
   return QSA_OK;
@@ -236,8 +252,7 @@ qsa_status qsa_decode(const qsa_geometry* g, const qsa_paged_cache* cache, int32
   // the indexer runs on the base position; draft positions reuse its selection
   QSA_HIP(launch_index_score_gemv(cache->khat, cache->page_table, cache->max_pages,
                                   cache->num_pages, batch, nullptr, ctx_lens, 0, 0,
-                                  max_ctx - (q_per_req - 1), q_idx, w_idx, scores, lay.gstride,
-                                  false, s));
+                                  max_ctx - (q_per_req - 1), q_idx, w_idx, scores, lay.gstride, s));
   QSA_HIP(launch_topk(scores, lay.gstride, batch, ctx_lens, 0, max_ctx - (q_per_req - 1),
                       g->topk_groups, sel, w + lay.off_topk, s));
   AttnArgs a = attn_args(g, cache);
@@ -276,9 +291,9 @@ qsa_status qsa_prefill(const qsa_geometry* g, const qsa_paged_cache* cache, int3
   char* w = (char*)ws;
   float* scores = out_scores ? out_scores : (float*)(w + lay.off_scores);
   int32_t* sel = out_groups ? out_groups : (int32_t*)(w + lay.off_sel);
-  QSA_HIP(launch_index_score_gemv(cache->khat, cache->page_table, cache->max_pages,
-                                  cache->num_pages, n_q, nullptr, nullptr, req, first_pos,
-                                  max_ctx, q_idx, w_idx, scores, lay.gstride, true, s));
+  QSA_HIP(launch_index_score_prefill(cache->khat, cache->page_table, cache->max_pages,
+                                     cache->num_pages, req, first_pos, n_q, q_idx, w_idx, scores,
+                                     lay.gstride, s));
   QSA_HIP(launch_topk(scores, lay.gstride, n_q, nullptr, first_pos, max_ctx, g->topk_groups, sel,
                       w + lay.off_topk, s));
   AttnArgs a = attn_args(g, cache);

@@ -11,13 +11,12 @@ namespace qsa {
 // (fp32 GEMV).  scores is [n_rows, gstride]; columns g >= floor(L/4) get
 // -inf.  Rows take (request, L) from row_req/row_len; with row_req null,
 // row r uses page-table row r; with both null, rows are queries
-// first_pos + row of request req0.  round_bf16 rounds
-// q_idx and k̂ to bf16 before the products.
+// first_pos + row of request req0.
 hipError_t launch_index_score_gemv(const float* khat, const int32_t* page_table, int max_pages,
                                    int num_pages, int n_rows, const int32_t* row_req,
                                    const int32_t* row_len, int req0, int first_pos, int max_ctx,
                                    const float* q_idx, const float* w_idx, float* scores,
-                                   int gstride, bool round_bf16, hipStream_t stream);
+                                   int gstride, hipStream_t stream);
 
 // Indexer scores of a prefill chunk on the matrix cores (bf16 operands,
 // fp32 accumulation): query i of the chunk has L = first_pos + i + 1.
