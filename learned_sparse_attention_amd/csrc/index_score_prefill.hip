@@ -297,15 +297,24 @@ __global__ __launch_bounds__(kPfThreads, 1) void index_score_mfma_kernel(
     pg_next = pg_after;
     __syncthreads();
   }
-  // ---- blocks past every query's causal limit: -inf only
-  if (q_ok) {
-    for (int gb = max(gb_begin, gb_live); gb < gb_end; ++gb) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int gq = gb * kPfGroups + 8 * k + 4 * hf;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (gq + i < gstride) srow[gq + i] = -INFINITY;
+  // ---- blocks past every query's causal limit: -inf only, written by the
+  // whole workgroup with row-contiguous stores
+  const int c0 = max(gb_begin, gb_live) * kPfGroups, c1 = min(gb_end * kPfGroups, gstride);
+  if (c0 < c1) {
+    const int row0 = qt * kPfQueries;
+    const int rows = min(kPfQueries, n_q - row0);
+    if (vec_ok) {
+      const int nf4 = (c1 - c0) / 4;
+      const float4 ninf = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      for (int idx = tid; idx < rows * nf4; idx += kPfThreads) {
+        const int r = idx / nf4, j = idx - r * nf4;
+        *reinterpret_cast<float4*>(scores + (size_t)(row0 + r) * gstride + c0 + 4 * j) = ninf;
+      }
+    } else {
+      const int n = c1 - c0;
+      for (int idx = tid; idx < rows * n; idx += kPfThreads) {
+        const int r = idx / n, j = idx - r * n;
+        scores[(size_t)(row0 + r) * gstride + c0 + j] = -INFINITY;
       }
     }
   }
