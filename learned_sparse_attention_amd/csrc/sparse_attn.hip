@@ -389,6 +389,12 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restri
   const float* p = partial + ((size_t)(b * Hkv + kvh) * n_splits) * split_stride +
                    (size_t)r * (2 + kHeadDim);
   const int t = threadIdx.x, lane = t & (kWave - 1), wid = t / kWave;
+  // the first kEarly splits' accumulators are fetched together with the
+  // (max, sum) pairs, so both come back in one memory round trip
+  constexpr int kEarly = 32;
+  float early[kEarly];
+#pragma unroll
+  for (int s = 0; s < kEarly; ++s) early[s] = s < n_splits ? p[s * split_stride + 2 + t] : 0.0f;
   const float m = t < n_splits ? p[t * split_stride] : -INFINITY;
   const float l = t < n_splits ? p[t * split_stride + 1] : 0.0f;
   float M = wave_max(m);
@@ -396,15 +402,17 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restri
   __syncthreads();
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float f = (m == -INFINITY) ? 0.0f : exp2f(m - M);
-  if (t < n_splits) fac[t] = f;
+  fac[t] = f;  // 0 for t >= n_splits (m = -inf there)
   __syncthreads();
   float den = wave_sum(f * l);
   if (lane == 0) red[wid] = den;  // (every thread has read red[] above)
   __syncthreads();
   den = (red[0] + red[1]) + (red[2] + red[3]);
   float num = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kEarly; ++s) num += fac[s] * early[s];  // fac[s] = 0 past n_splits
 #pragma unroll 8
-  for (int s = 0; s < n_splits; ++s) num += fac[s] * p[s * split_stride + 2 + t];
+  for (int s = kEarly; s < n_splits; ++s) num += fac[s] * p[s * split_stride + 2 + t];
   out[(((size_t)b * Q + j) * Hq + h) * kHeadDim + t] = den > 0.0f ? num * (v_scale / den) : 0.0f;
 }
 

@@ -420,6 +420,23 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
 
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
+  // Candidate slots and counts are fetched first, before the row length is
+  // known (every slot lies inside the workspace), so their latency overlaps
+  // the length load; slot m*NT + tid lies in slice m (kSliceCap == NT).
+  uint32_t ck[MC];
+  uint32_t cg[MC];
+  int cnt[MC];
+  if (kFromCand) {
+    static_assert(!kFromCand || kSliceCap == NT, "one slice per slot row");
+    static_assert(!kFromCand || MC == kMaxSlices, "one count per slot row");
+    const size_t base = (size_t)row * kMaxSlices * kSliceCap;
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      cnt[m] = cand_cnt[row * kMaxSlices + m];
+      ck[m] = cand_val[base + m * NT + tid];
+      cg[m] = cand_idx[base + m * NT + tid];
+    }
+  }
   const int L = row_len ? row_len[row] : first_pos + row + 1;
   int G = (L >= 0 && L <= max_ctx) ? L / kRatio : 0;
   if (G > gstride) G = gstride;
@@ -433,23 +450,11 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
   for (int i = tid; i < nwords; i += NT) { selmap[i] = 0u; eqmap[i] = 0u; }
 
   // candidates: slot m*NT + tid
-  uint32_t ck[MC];
-  uint32_t cg[MC];
   bool ok = true;
   if (kFromCand) {
-    // slot m*NT + tid lies in slice m (kSliceCap == NT): every load below is
-    // independent, so all of them are in flight together
-    static_assert(kSliceCap == NT, "one slice per slot row");
     const int n_slices = (G + kSlice - 1) / kSlice;
-    int cnt[MC];
 #pragma unroll
-    for (int m = 0; m < MC; ++m) cnt[m] = m < n_slices ? cand_cnt[row * kMaxSlices + m] : 0;
-    const size_t base = (size_t)row * kMaxSlices * kSliceCap;
-#pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      ck[m] = cand_val[base + m * NT + tid];
-      cg[m] = cand_idx[base + m * NT + tid];
-    }
+    for (int m = 0; m < MC; ++m) cnt[m] = m < n_slices ? cnt[m] : 0;
     uint32_t C = 0;
 #pragma unroll
     for (int m = 0; m < MC; ++m) {
