@@ -36,7 +36,8 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_gemv_kernel(
     const float* __restrict__ khat, const int32_t* __restrict__ page_table, int max_pages,
     int num_pages, const int32_t* __restrict__ row_req, const int32_t* __restrict__ row_len,
     int req0, int first_pos, int max_ctx, const float* __restrict__ q_idx,
-    const float* __restrict__ w_idx, float* __restrict__ scores, int gstride) {
+    const float* __restrict__ w_idx, float* __restrict__ scores, int gstride,
+    float* __restrict__ samples) {
   // rows carry their own (request, length); with row_req null, row r uses
   // page-table row r; with both null, rows are the consecutive queries of
   // request req0 starting at position first_pos
@@ -86,7 +87,16 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_gemv_kernel(
         if (g0 + (lane & 15) < G) sc = keep + 0.0f;  // -0 -> +0
       }
     }
-    if (lane < kGroupsPerPage && g0 + lane < gstride) srow[g0 + lane] = sc;
+    if (lane < kGroupsPerPage && g0 + lane < gstride) {
+      srow[g0 + lane] = sc;
+      // group g is sample i when floor(i * G / n) = g, i.e. i = ceil(g * n / G)
+      const int g = g0 + lane;
+      if (samples && G >= kTopkSamples && g < G) {
+        const int i = (int)(((long long)g * kTopkSamples + G - 1) / G);
+        if (i < kTopkSamples && (int)(((long long)i * G) / kTopkSamples) == g)
+          samples[(size_t)row * kTopkSamples + i] = sc;
+      }
+    }
   }
 }
 
@@ -96,13 +106,13 @@ hipError_t launch_index_score_gemv(const float* khat, const int32_t* page_table,
                                    int num_pages, int n_rows, const int32_t* row_req,
                                    const int32_t* row_len, int req0, int first_pos, int max_ctx,
                                    const float* q_idx, const float* w_idx, float* scores,
-                                   int gstride, hipStream_t stream) {
+                                   int gstride, hipStream_t stream, float* samples) {
   if (n_rows <= 0 || gstride <= 0) return hipSuccess;
   const int row_pages = (gstride + kGroupsPerPage - 1) / kGroupsPerPage;
   dim3 grid((row_pages + kPagesPerBlock - 1) / kPagesPerBlock, n_rows, 1);
   hipLaunchKernelGGL(index_score_gemv_kernel, grid, dim3(kScoreThreads), 0, stream, khat,
                      page_table, max_pages, num_pages, row_req, row_len, req0, first_pos, max_ctx,
-                     q_idx, w_idx, scores, gstride);
+                     q_idx, w_idx, scores, gstride, samples);
   return hipGetLastError();
 }
 

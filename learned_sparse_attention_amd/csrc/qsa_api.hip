@@ -38,7 +38,7 @@ int groups_per_split(const qsa_geometry* g, int batch, int q_per_req) {
 
 struct DecodeLayout {
   int gps, n_splits, gstride;
-  size_t off_scores, off_sel, off_partial, off_topk, total;
+  size_t off_scores, off_samples, off_sel, off_partial, off_topk, total;
 };
 
 DecodeLayout decode_layout(const qsa_geometry* g, int batch, int q_per_req, int max_ctx) {
@@ -50,6 +50,8 @@ DecodeLayout decode_layout(const qsa_geometry* g, int batch, int q_per_req, int 
   size_t off = 0;
   d.off_scores = off;
   off += align_up(sizeof(float) * (size_t)batch * d.gstride);
+  d.off_samples = off;
+  off += align_up(sizeof(float) * (size_t)batch * kTopkSamples);
   d.off_sel = off;
   off += align_up(sizeof(int32_t) * (size_t)batch * g->topk_groups);
   d.off_partial = off;
@@ -63,7 +65,7 @@ DecodeLayout decode_layout(const qsa_geometry* g, int batch, int q_per_req, int 
 
 struct RowsLayout {
   int gstride;
-  size_t off_scores, off_sel, off_topk, total;
+  size_t off_scores, off_samples, off_sel, off_topk, total;
 };
 
 RowsLayout rows_layout(const qsa_geometry* g, int n_rows, int max_ctx) {
@@ -72,6 +74,8 @@ RowsLayout rows_layout(const qsa_geometry* g, int n_rows, int max_ctx) {
   size_t off = 0;
   r.off_scores = off;
   off += align_up(sizeof(float) * (size_t)n_rows * r.gstride);
+  r.off_samples = off;
+  off += align_up(sizeof(float) * (size_t)n_rows * kTopkSamples);
   r.off_sel = off;
   off += align_up(sizeof(int32_t) * (size_t)n_rows * g->topk_groups);
   r.off_topk = off;
@@ -221,11 +225,12 @@ qsa_status qsa_index_topk(const qsa_geometry* g, const qsa_paged_cache* cache, i
   if ((st = ws_ok(ws, ws_bytes, lay.total)) != QSA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   float* scores = out_scores ? out_scores : (float*)((char*)ws + lay.off_scores);
+  float* samples = (float*)((char*)ws + lay.off_samples);
   QSA_HIP(launch_index_score_gemv(cache->khat, cache->page_table, cache->max_pages,
                                   cache->num_pages, n_rows, row_req, row_len, 0, 0, max_ctx,
-                                  q_idx, w_idx, scores, lay.gstride, s));
+                                  q_idx, w_idx, scores, lay.gstride, s, samples));
   QSA_HIP(launch_topk(scores, lay.gstride, n_rows, row_len, 0, max_ctx, g->topk_groups,
-                      out_groups, (char*)ws + lay.off_topk, s));
+                      out_groups, (char*)ws + lay.off_topk, s, samples));
   return QSA_OK;
 }
 
@@ -249,12 +254,14 @@ qsa_status qsa_decode(const qsa_geometry* g, const qsa_paged_cache* cache, int32
   char* w = (char*)ws;
   float* scores = out_scores ? out_scores : (float*)(w + lay.off_scores);
   int32_t* sel = out_groups ? out_groups : (int32_t*)(w + lay.off_sel);
+  float* samples = (float*)(w + lay.off_samples);
   // the indexer runs on the base position; draft positions reuse its selection
   QSA_HIP(launch_index_score_gemv(cache->khat, cache->page_table, cache->max_pages,
                                   cache->num_pages, batch, nullptr, ctx_lens, 0, 0,
-                                  max_ctx - (q_per_req - 1), q_idx, w_idx, scores, lay.gstride, s));
+                                  max_ctx - (q_per_req - 1), q_idx, w_idx, scores, lay.gstride, s,
+                                  samples));
   QSA_HIP(launch_topk(scores, lay.gstride, batch, ctx_lens, 0, max_ctx - (q_per_req - 1),
-                      g->topk_groups, sel, w + lay.off_topk, s));
+                      g->topk_groups, sel, w + lay.off_topk, s, samples));
   AttnArgs a = attn_args(g, cache);
   a.sel = sel;
   a.ctx_lens = ctx_lens;

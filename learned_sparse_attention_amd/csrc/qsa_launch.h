@@ -11,12 +11,16 @@ namespace qsa {
 // (fp32 GEMV).  scores is [n_rows, gstride]; columns g >= floor(L/4) get
 // -inf.  Rows take (request, L) from row_req/row_len; with row_req null,
 // row r uses page-table row r; with both null, rows are queries
-// first_pos + row of request req0.
+// first_pos + row of request req0.  If samples is non-null and a row has
+// G >= kTopkSamples groups, the kernel also writes that row's scores of
+// groups floor(i * G / kTopkSamples), i < kTopkSamples, to
+// samples[row * kTopkSamples + i] (the top-K's pruning sample).
+constexpr int kTopkSamples = 512;
 hipError_t launch_index_score_gemv(const float* khat, const int32_t* page_table, int max_pages,
                                    int num_pages, int n_rows, const int32_t* row_req,
                                    const int32_t* row_len, int req0, int first_pos, int max_ctx,
                                    const float* q_idx, const float* w_idx, float* scores,
-                                   int gstride, hipStream_t stream);
+                                   int gstride, hipStream_t stream, float* samples = nullptr);
 
 // Indexer scores of a prefill chunk on the matrix cores (bf16 operands,
 // fp32 accumulation): query i of the chunk has L = first_pos + i + 1.
@@ -30,9 +34,10 @@ hipError_t launch_index_score_prefill(const float* khat, const int32_t* page_tab
 // L = first_pos + row + 1.  out is [n_rows, K] ascending, -1 padded.  ws
 // (256-byte aligned, topk_workspace_bytes) holds candidates of long rows.
 size_t topk_workspace_bytes(int n_rows, int gstride);
+// samples (nullable): the scoring kernel's per-row pruning sample.
 hipError_t launch_topk(const float* scores, int gstride, int n_rows, const int32_t* row_len,
                        int first_pos, int max_ctx, int K, int32_t* out, void* ws,
-                       hipStream_t stream);
+                       hipStream_t stream, const float* samples = nullptr);
 
 struct AttnArgs {
   const void* k;

@@ -313,7 +313,9 @@ __device__ uint32_t exact_threshold_stream(const float* srow, int G, uint32_t ne
 __global__ __launch_bounds__(kExtractThreads) void topk_extract_kernel(
     const float* __restrict__ scores, int gstride, const int32_t* __restrict__ row_len,
     int first_pos, int max_ctx, int K, uint32_t* __restrict__ cand_val,
-    uint16_t* __restrict__ cand_idx, int32_t* __restrict__ cand_cnt) {
+    uint16_t* __restrict__ cand_idx, int32_t* __restrict__ cand_cnt,
+    const float* __restrict__ samples) {
+  static_assert(kSample == kTopkSamples, "one sample layout");
   constexpr int NT = kExtractThreads, NW = NT / kWave;
   constexpr int E4 = kSlice / (4 * NT);  // float4 chunks per thread
   constexpr int kCW = kSliceCap / NW;    // slots per wave
@@ -325,39 +327,53 @@ __global__ __launch_bounds__(kExtractThreads) void topk_extract_kernel(
 
   const int slice = blockIdx.x, row = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  const int L = row_len ? row_len[row] : first_pos + row + 1;
-  int G = (L >= 0 && L <= max_ctx) ? L / kRatio : 0;
-  if (G > gstride) G = gstride;
   const size_t slot0 = ((size_t)row * kMaxSlices + slice) * kSliceCap;
   const int g0 = slice * kSlice;
-  if (G <= K || g0 >= G) {  // finish handles the row alone / empty slice
-    if (tid == 0) cand_cnt[row * kMaxSlices + slice] = 0;
-    return;
-  }
   const float* srow = scores + (size_t)row * gstride;
 
-  // slice loads (in flight while wave 0 derives the guess)
+  // Slice loads and the scoring kernel's sample are issued before the row
+  // length is known (both stay inside their rows), so their latency
+  // overlaps the length load; entries past the row's groups are masked
+  // once it is.
   uint32_t v[4 * E4];
 #pragma unroll
   for (int e = 0; e < E4; ++e) {
     const int c0 = g0 + 4 * (e * NT + tid);
-    if (((reinterpret_cast<uintptr_t>(srow) & 15u) == 0u) && c0 + 3 < G) {
+    if (((reinterpret_cast<uintptr_t>(srow) & 15u) == 0u) && c0 + 3 < gstride) {
       const float4 f = *reinterpret_cast<const float4*>(srow + c0);
       v[4 * e] = __float_as_uint(f.x); v[4 * e + 1] = __float_as_uint(f.y);
       v[4 * e + 2] = __float_as_uint(f.z); v[4 * e + 3] = __float_as_uint(f.w);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        v[4 * e + j] = c0 + j < G ? __float_as_uint(srow[c0 + j]) : 0x7FC00000u;  // NaN: never kept
+        v[4 * e + j] = c0 + j < gstride ? __float_as_uint(srow[c0 + j]) : 0x7FC00000u;
     }
   }
+  float sv[8];
+  if (samples && wid == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sv[i] = samples[(size_t)row * kSample + lane + kWave * i];
+  }
+  const int L = row_len ? row_len[row] : first_pos + row + 1;
+  int G = (L >= 0 && L <= max_ctx) ? L / kRatio : 0;
+  if (G > gstride) G = gstride;
+  if (G <= K || g0 >= G) {  // finish handles the row alone / empty slice
+    if (tid == 0) cand_cnt[row * kMaxSlices + slice] = 0;
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < E4; ++e)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (g0 + 4 * (e * NT + tid) + j >= G) v[4 * e + j] = 0x7FC00000u;  // NaN: never kept
 
   if (wid == 0) {
     uint32_t sk[8];
+    const bool have = samples && G >= kSample;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int si = (int)(((long long)(lane + kWave * i) * G) / kSample);
-      sk[i] = score_key(srow[si]);
+      sk[i] = score_key(have ? sv[i] : srow[si]);
     }
     const int r0 = (int)(((long long)kSample * K + G - 1) / G);
     int r = r0 + 4 * (int)ceilf(sqrtf((float)r0)) + 4;
@@ -538,7 +554,7 @@ size_t topk_workspace_bytes(int n_rows, int gstride) {
 
 hipError_t launch_topk(const float* scores, int gstride, int n_rows, const int32_t* row_len,
                        int first_pos, int max_ctx, int K, int32_t* out, void* ws,
-                       hipStream_t stream) {
+                       hipStream_t stream, const float* samples) {
   if (n_rows <= 0) return hipSuccess;
   if (gstride > kMaxGroups) return hipErrorInvalidValue;
   if (gstride <= kDirect) {
@@ -557,7 +573,8 @@ hipError_t launch_topk(const float* scores, int gstride, int n_rows, const int32
   int32_t* ccnt = reinterpret_cast<int32_t*>(p);
   const int n_slices = (gstride + kSlice - 1) / kSlice;
   hipLaunchKernelGGL(topk_extract_kernel, dim3(n_slices, n_rows), dim3(kExtractThreads), 0,
-                     stream, scores, gstride, row_len, first_pos, max_ctx, K, cval, cidx, ccnt);
+                     stream, scores, gstride, row_len, first_pos, max_ctx, K, cval, cidx, ccnt,
+                     samples);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((topk_finish_kernel<true, kMaxSlices * kSliceCap / kFinishThreads>),
