@@ -8,7 +8,9 @@ Inputs are seeded and synthetic and resident in HBM before timing.
 
 Prints one JSON line: layer-steps/s, the roofline position of the dominant
 kernel (the indexer GEMV, HBM-bound) measured with HIP events on the stream
-it runs on, and the CPU oracle timed on this host as a reported baseline.
+it runs on, the prefill indexer scoring on the matrix cores against the BF16
+MFMA peak (the long-prefill chunk), and the CPU oracle timed on this host as
+a reported baseline.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
 """
@@ -169,6 +171,65 @@ def write_counters(fetch_dir: str, write_dir: str, workload_name: str, commands:
     print(json.dumps(rec))
 
 
+def prefill_scoring(dev, steps: int, warmup: int) -> dict:
+    """The long-prefill chunk (4,096 queries at positions 28,672 .. 32,767 of
+    one request, 8,192 groups): the matrix-core indexer scoring alone, timed
+    with events on the stream it runs on, against the dense BF16 MFMA peak;
+    and the whole qsa_prefill step (scoring, top-K, attention) for context."""
+    import numpy as np
+    import torch
+    import learned_sparse_attention_amd as qsa
+    import workload
+    from tests import qsa_gpu as H
+    wl = workload.config(4)
+    d = H.to_dev(wl, dev)
+    g = wl.geom
+    gstride = (wl.first_pos + wl.n_q) // 4
+    sc = torch.empty((wl.n_q, gstride), dtype=torch.float32, device=dev)
+
+    def score():
+        qsa.qsa_index_score_prefill(g, d["khat"], d["pt"], wl.req, wl.first_pos, d["q_idx"],
+                                    d["w_idx"], out_scores=sc, num_pages=wl.num_pages)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(warmup):
+        score()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        score()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    visible = int((wl.row_len.astype(np.int64) // 4).sum()) * 2 * 8 * 64
+    dense = wl.n_q * gstride * 2 * 8 * 64
+    out = torch.empty((wl.n_q, g["num_q_heads"], g["head_dim"]), dtype=torch.float32, device=dev)
+    ws = torch.empty(qsa.prefill_workspace_size(g, wl.n_q, wl.first_pos + wl.n_q),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        qsa.qsa_prefill(g, d["k"], d["v"], d["khat"], d["pt"], wl.req, wl.first_pos, d["q_idx"],
+                        d["w_idx"], d["q"], out=out, workspace=ws, num_pages=wl.num_pages)
+
+    step()
+    torch.cuda.synchronize()
+    n_step = max(1, steps // 10)
+    e0.record()
+    for _ in range(n_step):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / n_step
+    tflops = visible / (ms * 1e-3) / 1e12
+    return {"workload": "prefill chunk of 4,096 queries at positions 28,672..32,767, "
+                        "8,192 groups, 8 heads x 64, BF16 KV, K=512 groups",
+            "kernel": "index_score_mfma_kernel", "bound": "mfma", "achieved": tflops,
+            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS,
+            "flops_per_launch": visible, "dense_tile_flops": dense, "ms_per_launch": ms,
+            "score_bytes_written": wl.n_q * gstride * 4,
+            "prefill_step_ms": ms_step}
+
+
 def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
     """The oracle, unchanged, on this host: full decode steps of a bounded
     subset of requests, scaled to layer-steps/s of the whole batch."""
@@ -197,6 +258,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill-scoring measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also launch a 1 GiB copy kernel (for counter runs)")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -299,6 +362,8 @@ def main() -> int:
                           "frac": step_gbs / HBM_PEAK_GBS},
         "gen_seconds": round(t_gen, 1),
     }
+    if not args.no_prefill:
+        result["prefill_scoring"] = prefill_scoring(dev, max(5, args.steps // 2), 3)
     if args.calibrate_copy:
         calibrate_copy(dev)
     if not args.no_cpu_baseline:
