@@ -68,21 +68,20 @@ def test_prefill_scores_equal_inside_prefill(gpu):
 
 def _sample_rows(n_q, seed):
     fixed = [0, 1, 2, 3, 31, 32, 255, 256, 257, 1023, 1024, 2047, 2048, 3071, 3072, 4064, 4093,
-             4094, 4095]
+             4094, 4095, n_q - 2, n_q - 1]
     rng = np.random.default_rng(seed)
     extra = rng.choice(n_q, 16, replace=False).tolist()
-    return np.array(sorted(set(r for r in fixed + extra if r < n_q)))
+    return np.array(sorted(set(r for r in fixed + extra if 0 <= r < n_q)))
 
 
-def test_prefill_long_chunk_sampled(gpu):
-    # the long-prefill chunk at full size, in the launch configuration the
-    # benchmark times; checked on sampled query rows the oracle computes
+def _prefill_check(wl, gpu, rows):
+    """qsa_prefill on the whole chunk; scores, top-K, token lists and
+    attention compared with the oracle on `rows`; the -inf mask on every
+    row; every output finite."""
     import torch
-    wl = workload.config(4)
     d = H.to_dev(wl, gpu)
     res = H.run_prefill(wl, d)
     torch.cuda.synchronize()
-    rows = _sample_rows(wl.n_q, 4)
     r = oracle.prefill(wl, rows=rows)
     gs = res["scores"].cpu().numpy()
     G = (wl.row_len[rows] // 4).astype(np.int32)
@@ -96,10 +95,37 @@ def test_prefill_long_chunk_sampled(gpu):
     W = oracle.token_width(K)
     for i, p in enumerate(rows):
         assert np.array_equal(gt[i], oracle.position_tokens(gg[i], int(wl.row_len[p]), 0, W))
+    out = res["out"].cpu().numpy()
+    assert np.all(np.isfinite(out))
     ora_o = oracle.attend(wl.geom, wl.row_req[rows], gt, wl.q[rows], wl.k_cache, wl.v_cache,
                           wl.page_table, wl.num_pages)
-    H.check_attention(res["out"].cpu().numpy()[rows], ora_o, 0)
+    H.check_attention(out[rows], ora_o, 0 if wl.geom["kv_dtype"] == 0 else 1)
     # every row's scores, not only the sampled ones: -inf exactly past G
     Gall = wl.row_len // 4
     cols = np.arange(gstride)[None, :]
     assert np.array_equal(np.isneginf(gs), cols >= Gall[:, None])
+
+
+def test_prefill_long_chunk_sampled(gpu):
+    # the long-prefill chunk at full size, in the launch configuration the
+    # benchmark times; checked on sampled query rows the oracle computes
+    wl = workload.config(4)
+    _prefill_check(wl, gpu, _sample_rows(wl.n_q, 4))
+
+
+def test_prefill_long_7810_queries_over_65536(gpu):
+    # the operator suite's long-prefill case (PR #41855 article, Tests):
+    # 7,810 queries ending a 65,536-token cache, 2,051 selected slots each
+    # (K = 512 groups plus the current block), on sampled rows
+    wl = workload.prefill_workload(830, 65536 - 7810, 7810, kv_dtype="bf16", topk_groups=512)
+    assert 4 * wl.geom["topk_groups"] + 3 == 2051
+    _prefill_check(wl, gpu, _sample_rows(wl.n_q, 5))
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 2), (24, 2), (12, 1), (6, 1), (3, 1)])
+@pytest.mark.parametrize("n_q,kv", [(1, "fp8"), (257, "bf16")])
+def test_prefill_head_shapes(gpu, hq, hkv, n_q, kv):
+    # the operator suite's local head shapes at 1 and 257 query rows
+    wl = workload.prefill_workload(840 + 7 * hq + hkv + n_q, 2500, n_q, num_q_heads=hq,
+                                   num_kv_heads=hkv, kv_dtype=kv, topk_groups=512)
+    _prefill_check(wl, gpu, np.arange(n_q))
