@@ -66,6 +66,10 @@ def lib():
         L.qo_attend.argtypes = [i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, dbl, dbl, dbl,
                                 vp, i32, i32, vp, vp]
         L.qo_num_threads.restype = i32
+        L.qo_fp8_e4m3_encode.restype = ctypes.c_uint8
+        L.qo_fp8_e4m3_encode.argtypes = [dbl]
+        L.qo_append.argtypes = [i32, vp, vp, i32, i32, i32, i32, dbl, dbl, vp, vp, vp, i32, i32,
+                                i32, vp, vp, vp, vp, i32, i32, i32, i32]
         _lib = L
     return _lib
 
@@ -86,6 +90,11 @@ def num_threads() -> int:
 
 def fp8_e4m3_value(code: int) -> float:
     return float(lib().qo_fp8_e4m3(int(code)))
+
+
+def fp8_e4m3_encode(x: float) -> int:
+    """Nearest E4M3FN code, ties to the even mantissa, saturating at 448."""
+    return int(lib().qo_fp8_e4m3_encode(float(x)))
 
 
 def bf16_value(bits: int) -> float:
@@ -230,3 +239,36 @@ def dense(geom, req: int, L: int, q_rows, k_cache, v_cache, page_table, num_page
     toks = np.tile(np.arange(L, dtype=np.int32), (q_rows.shape[0], 1))
     return attend(geom, np.full(q_rows.shape[0], req, np.int32), toks, q_rows, k_cache, v_cache,
                   page_table, num_pages)
+
+
+# --- cache append (the "prefill writes" of the KV and k-hat caches) --------
+
+def append_khat_slots(n_tokens: int) -> int:
+    """k-hat slots per request of an append: groups completed by n_tokens
+    new tokens, at most floor((n_tokens + 3) / 4)."""
+    return (n_tokens + RATIO - 1) // RATIO
+
+
+def append(geom: dict, k_cache, v_cache, khat, page_table, num_pages: int, req_rows, start_pos,
+           k_new, v_new, khat_new=None):
+    """Write the new tokens' K/V (bf16 [n_req, n, Hkv, D]) and the
+    completed groups' k-hat into copies of the caches; returns
+    (k_cache, v_cache, khat).  See qo_append."""
+    L = lib()
+    kc, vc, kh = k_cache.copy(), v_cache.copy(), khat.copy()
+    pt = _c(page_table, np.int32)
+    rr, sp = _c(req_rows, np.int32), _c(start_pos, np.int32)
+    kn, vn = _c(k_new, np.uint16), _c(v_new, np.uint16)
+    n_req, n_tok = kn.shape[0], kn.shape[1]
+    slots = append_khat_slots(n_tok)
+    if khat_new is not None:
+        khn = _c(khat_new, np.float32)
+        assert khn.shape[:2] == (n_req, slots)
+        khp = _p(khn)
+    else:
+        khp = None
+    L.qo_append(n_req, _p(rr), _p(sp), n_tok, geom["num_kv_heads"], geom["head_dim"],
+                geom["kv_dtype"], geom["k_scale"], geom["v_scale"], _p(kn), _p(vn), khp, slots,
+                kh.shape[2], kh.shape[3], _p(kc), _p(vc), _p(kh), _p(pt), pt.shape[1],
+                int(num_pages), PAGE, RATIO)
+    return kc, vc, kh

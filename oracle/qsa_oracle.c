@@ -75,12 +75,105 @@ float qo_round_bf16(float x) {
   return r;
 }
 
+static int page_ok(int32_t p, int num_pages) { return p >= 0 && p < num_pages; }
+
+/* Nearest OCP E4M3FN code to x (the format above): the finite code whose
+ * value is closest to x; on a tie, the code with an even mantissa field;
+ * magnitudes beyond the largest finite value saturate to +-448 (the
+ * library's reading: the pages name FP8 E4M3 KV but not an overflow rule);
+ * NaN gives 0x7F.  Found by scanning all non-negative finite codes. */
+uint8_t qo_fp8_e4m3_encode(double x) {
+  if (x != x) return 0x7F;
+  const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  const double a = fabs(x);
+  if (a > 448.0) return (uint8_t)(sign | 0x7E); /* saturation, infinities included */
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    const double err = fabs(qo_fp8_e4m3((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+/* Nearest bfloat16 to a binary32 value, ties to even (bits). */
+static uint16_t bf16_bits_rne(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  if (x != x) return (uint16_t)((u >> 16) | 0x40u);
+  u = u + 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+/* One stored K or V element for the new value x (a bfloat16) and the
+ * per-tensor scale s of the cache: the binary32 quotient x / s (correctly
+ * rounded), then its nearest FP8 E4M3 code, or its nearest bfloat16 for a
+ * BF16 cache (x itself when s == 1).  Reading: the pages name FP8 E4M3 KV
+ * with "prefill writes" (qsa-hisparse README, offload contract and entry
+ * points) but print no quantiser; the per-tensor scale is the one the
+ * attention decodes with.  The quotient of two binary32 values taken in
+ * binary64 and then rounded to binary32 is the correctly rounded binary32
+ * quotient (53 >= 2 * 24 + 2 bits, so the double rounding is innocuous). */
+static void store_kv(void* cache, int kv_dtype, int64_t index, uint16_t x_bits, double scale) {
+  const float q = (float)(qo_bf16(x_bits) / scale);
+  if (kv_dtype == 0)
+    ((uint16_t*)cache)[index] = bf16_bits_rne(q);
+  else
+    ((uint8_t*)cache)[index] = qo_fp8_e4m3_encode((double)q);
+}
+
+/* Append n_tokens new tokens to each of n_req requests.  Request r uses
+ * page-table row req_rows[r]; its new tokens take positions
+ * start_pos[r] .. start_pos[r] + n_tokens - 1, token t landing in page
+ * page_table[row][t / page_size], slot t % page_size.  k_new / v_new are
+ * [n_req, n_tokens, Hkv, D] bfloat16.  khat_new (may be NULL) is
+ * [n_req, khat_slots, Hi, Di] fp32: slot j holds group
+ * floor(start_pos[r] / ratio) + j, and is written when that group's last
+ * token (ratio * g + ratio - 1) is among the appended ones.  Positions
+ * whose page-table entry lies outside the row or names a page outside
+ * [0, num_pages) are not written. */
+void qo_append(int n_req, const int32_t* req_rows, const int32_t* start_pos, int n_tokens, int Hkv,
+               int D, int kv_dtype, double k_scale, double v_scale, const uint16_t* k_new,
+               const uint16_t* v_new, const float* khat_new, int khat_slots, int Hi, int Di,
+               void* k_cache, void* v_cache, float* khat_cache, const int32_t* page_table,
+               int max_pages, int num_pages, int page_size, int ratio) {
+  const int gpp = page_size / ratio;
+  for (int r = 0; r < n_req; ++r) {
+    const int32_t* pt = page_table + (int64_t)req_rows[r] * max_pages;
+    for (int i = 0; i < n_tokens; ++i) {
+      const int64_t t = (int64_t)start_pos[r] + i;
+      if (t < 0 || t / page_size >= max_pages) continue;
+      const int32_t p = pt[t / page_size];
+      if (!page_ok(p, num_pages)) continue;
+      const int64_t row = ((int64_t)p * page_size + t % page_size) * Hkv * D;
+      const int64_t src = ((int64_t)r * n_tokens + i) * Hkv * D;
+      for (int e = 0; e < Hkv * D; ++e) {
+        store_kv(k_cache, kv_dtype, row + e, k_new[src + e], k_scale);
+        store_kv(v_cache, kv_dtype, row + e, v_new[src + e], v_scale);
+      }
+    }
+    if (khat_new == NULL) continue;
+    const int64_t g0 = (int64_t)floor((double)start_pos[r] / ratio);
+    for (int j = 0; j < khat_slots; ++j) {
+      const int64_t g = g0 + j, last = g * ratio + ratio - 1;
+      if (g < 0 || last < start_pos[r] || last >= (int64_t)start_pos[r] + n_tokens) continue;
+      if (g / gpp >= max_pages) continue;
+      const int32_t p = pt[g / gpp];
+      if (!page_ok(p, num_pages)) continue;
+      memcpy(khat_cache + ((int64_t)p * gpp + g % gpp) * Hi * Di,
+             khat_new + ((int64_t)r * khat_slots + j) * Hi * Di, sizeof(float) * Hi * Di);
+    }
+  }
+}
+
 static double kv_value(const void* cache, int kv_dtype, int64_t index) {
   if (kv_dtype == 0) return qo_bf16(((const uint16_t*)cache)[index]);
   return qo_fp8_e4m3(((const uint8_t*)cache)[index]);
 }
 
-static int page_ok(int32_t p, int num_pages) { return p >= 0 && p < num_pages; }
 
 /* ---------------------------------------------------------------------- */
 /* Step 1: indexer scores                                                 */
