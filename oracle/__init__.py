@@ -267,8 +267,10 @@ def append(geom: dict, k_cache, v_cache, khat, page_table, num_pages: int, req_r
         khp = _p(khn)
     else:
         khp = None
+    # the geometry carries the scales as binary32 values
+    ks, vs = float(np.float32(geom["k_scale"])), float(np.float32(geom["v_scale"]))
     L.qo_append(n_req, _p(rr), _p(sp), n_tok, geom["num_kv_heads"], geom["head_dim"],
-                geom["kv_dtype"], geom["k_scale"], geom["v_scale"], _p(kn), _p(vn), khp, slots,
+                geom["kv_dtype"], ks, vs, _p(kn), _p(vn), khp, slots,
                 kh.shape[2], kh.shape[3], _p(kc), _p(vc), _p(kh), _p(pt), pt.shape[1],
                 int(num_pages), PAGE, RATIO)
     return kc, vc, kh

@@ -120,7 +120,7 @@ static uint16_t bf16_bits_rne(float x) {
 static void store_kv(void* cache, int kv_dtype, int64_t index, uint16_t x_bits, double scale) {
   const float q = (float)(qo_bf16(x_bits) / scale);
   if (kv_dtype == 0)
-    ((uint16_t*)cache)[index] = bf16_bits_rne(q);
+    ((uint16_t*)cache)[index] = scale == 1.0 ? x_bits : bf16_bits_rne(q);
   else
     ((uint8_t*)cache)[index] = qo_fp8_e4m3_encode((double)q);
 }
