@@ -254,6 +254,53 @@ qsa_status qsa_prefill(const qsa_geometry* g, const qsa_paged_cache* cache,
                        int32_t* out_tokens, float* out_scores, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* Number of k̂ slots per request that qsa_append_kv reads from khat_new for
+ * n_tokens new tokens: floor((n_tokens + 3) / 4), the most groups that
+ * many tokens can complete.  Returns 0 for n_tokens <= 0. */
+int32_t qsa_append_khat_slots(int32_t n_tokens);
+
+/* Cache append: the "prefill writes" of the attention backend (qsa-hisparse
+ * README, entry points), in the cache format of the offload contract (FP8
+ * E4M3 KV, page size 64).  Writes the keys and values of n_tokens new
+ * tokens of each of n_req requests into the paged KV cache, and the
+ * compressed indexer keys of the groups those tokens complete into the
+ * paged k̂ cache.  The compressor that produces k̂ is learned and not part
+ * of the library, so the caller supplies k̂.
+ *
+ *   n_req, n_tokens  host; >= 0.
+ *   k_cache, v_cache, khat_cache  the caches of qsa_paged_cache (written;
+ *             layouts as there); page_table [rows, max_pages] int32 with
+ *             max_pages, num_pages host, as in qsa_paged_cache.
+ *   req_rows  [n_req] int32: page-table row of each request.
+ *   start_pos [n_req] int32: position of each request's first new token.
+ *             New token i of request r is t = start_pos[r] + i and lands
+ *             in page page_table[row][t / page_size], slot t % page_size.
+ *   k_new, v_new [n_req, n_tokens, Hkv, D] bf16 bit patterns.  A stored
+ *             element is the binary32 quotient x / k_scale (v_scale for V),
+ *             correctly rounded, then rounded to the nearest FP8 E4M3FN
+ *             code (ties to an even mantissa; magnitudes above 448
+ *             saturate to +-448; NaN stays NaN) for an FP8 cache, or to the
+ *             nearest bfloat16 (ties to even) for a BF16 cache, which is x
+ *             itself when the scale is 1.  The pages print no quantiser;
+ *             this is the library's reading.
+ *   khat_new  nullable [n_req, qsa_append_khat_slots(n_tokens), H_i, D_i]
+ *             f32.  Slot j of request r holds group
+ *             g = floor(start_pos[r] / 4) + j.  It is written (copied) when
+ *             that group's last token 4g + 3 is among the new tokens.
+ * Tokens and groups at negative positions, at page-table indices
+ * >= max_pages, or on page ids outside [0, num_pages) are skipped.  New
+ * tokens of different requests that map to the same page slot race (a
+ * valid page table gives requests distinct pages).  Ordering against other
+ * calls that read the caches is the caller's, through `stream`.
+ */
+qsa_status qsa_append_kv(const qsa_geometry* g, void* k_cache, void* v_cache,
+                         float* khat_cache, const int32_t* page_table,
+                         int32_t max_pages, int32_t num_pages, int32_t n_req,
+                         const int32_t* req_rows, const int32_t* start_pos,
+                         int32_t n_tokens, const uint16_t* k_new,
+                         const uint16_t* v_new, const float* khat_new,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

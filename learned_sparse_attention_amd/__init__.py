@@ -84,6 +84,10 @@ def load():
         L.qsa_decode.argtypes = [G, C, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.qsa_prefill.restype = ctypes.c_int
         L.qsa_prefill.argtypes = [G, C, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.qsa_append_khat_slots.restype = i32
+        L.qsa_append_khat_slots.argtypes = [i32]
+        L.qsa_append_kv.restype = ctypes.c_int
+        L.qsa_append_kv.argtypes = [G, vp, vp, vp, vp, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -269,3 +273,29 @@ def qsa_prefill(geom, k_cache, v_cache, khat, page_table, req, first_pos, q_idx,
                               _ptr(scores), _ptr(ws), wsb, _stream(dev))
     _check("qsa_prefill", code)
     return dict(out=out, groups=groups, tokens=tokens, scores=scores)
+
+
+def append_khat_slots(n_tokens: int) -> int:
+    return int(load().qsa_append_khat_slots(int(n_tokens)))
+
+
+def qsa_append_kv(geom, k_cache, v_cache, khat_cache, page_table, req_rows, start_pos, k_new,
+                  v_new, khat_new=None, num_pages=None):
+    """Cache append, in place: the new tokens' K/V (bf16 bit patterns
+    [n_req, n_tokens, Hkv, D]) are stored in the cache format at positions
+    start_pos[r] + i of page-table row req_rows[r]; khat_new (optional,
+    [n_req, append_khat_slots(n_tokens), 8, 64] f32) fills the groups those
+    tokens complete.  The caches must be contiguous device tensors."""
+    for t in (k_cache, v_cache, khat_cache, page_table):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("caches and page table must be contiguous (written in place)")
+    dev = k_new.device
+    n_req, n_tok = int(k_new.shape[0]), int(k_new.shape[1])
+    npg = int(num_pages if num_pages is not None else k_cache.shape[0])
+    g = _geom(geom)
+    ins = [_c(req_rows), _c(start_pos), _c(k_new), _c(v_new), _c(khat_new)]
+    code = load().qsa_append_kv(ctypes.byref(g), _ptr(k_cache), _ptr(v_cache), _ptr(khat_cache),
+                                _ptr(page_table), int(page_table.shape[1]), npg, n_req,
+                                _ptr(ins[0]), _ptr(ins[1]), n_tok, _ptr(ins[2]), _ptr(ins[3]),
+                                _ptr(ins[4]), _stream(dev))
+    _check("qsa_append_kv", code)

@@ -319,4 +319,28 @@ qsa_status qsa_prefill(const qsa_geometry* g, const qsa_paged_cache* cache, int3
   return QSA_OK;
 }
 
+int32_t qsa_append_khat_slots(int32_t n_tokens) {
+  return n_tokens > 0 ? (n_tokens + kRatio - 1) / kRatio : 0;
+}
+
+qsa_status qsa_append_kv(const qsa_geometry* g, void* k_cache, void* v_cache, float* khat_cache,
+                         const int32_t* page_table, int32_t max_pages, int32_t num_pages,
+                         int32_t n_req, const int32_t* req_rows, const int32_t* start_pos,
+                         int32_t n_tokens, const uint16_t* k_new, const uint16_t* v_new,
+                         const float* khat_new, void* stream) {
+  qsa_status st = qsa_validate(g);
+  if (st != QSA_OK) return st;
+  if (n_req < 0 || n_tokens < 0 || max_pages < 1 || num_pages < 0) return QSA_ERR_INVALID_ARG;
+  if (n_req == 0 || n_tokens == 0) return QSA_OK;
+  if (!k_cache || !v_cache || !page_table || !req_rows || !start_pos || !k_new || !v_new)
+    return QSA_ERR_INVALID_ARG;
+  if (khat_new && !khat_cache) return QSA_ERR_INVALID_ARG;
+  if (!(g->k_scale > 0.0f) || !(g->v_scale > 0.0f)) return QSA_ERR_INVALID_ARG;
+  QSA_HIP(launch_append(k_cache, v_cache, khat_cache, page_table, max_pages, num_pages, n_req,
+                        req_rows, start_pos, n_tokens, k_new, v_new, khat_new,
+                        g->num_kv_heads * g->head_dim, g->kv_dtype, g->k_scale, g->v_scale,
+                        (hipStream_t)stream));
+  return QSA_OK;
+}
+
 }  // extern "C"

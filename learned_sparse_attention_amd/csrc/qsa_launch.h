@@ -66,6 +66,16 @@ struct AttnArgs {
 hipError_t launch_sparse_attn_decode(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_sparse_attn_prefill(const AttnArgs& a, hipStream_t stream);
 
+// Cache append: K/V of n_tokens new tokens per request (bf16 in, stored in
+// the cache format with the per-tensor scales) and the k̂ of the groups they
+// complete (khat_new nullable, (n_tokens + 3) / 4 slots per request).
+hipError_t launch_append(void* k_cache, void* v_cache, float* khat_cache,
+                         const int32_t* page_table, int max_pages, int num_pages, int n_req,
+                         const int32_t* req_rows, const int32_t* start_pos, int n_tokens,
+                         const uint16_t* k_new, const uint16_t* v_new, const float* khat_new,
+                         int row_elems, int kv_dtype, float k_scale, float v_scale,
+                         hipStream_t stream);
+
 // Expanded token lists: [rows, q_per_req, width], ascending, -1 padded.
 hipError_t launch_expand_tokens(const int32_t* sel, int K, int n_rows, int q_per_req,
                                 const int32_t* ctx_lens, int first_pos, int max_ctx, int width,

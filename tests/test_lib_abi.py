@@ -65,3 +65,24 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert lib.qsa_decode(ctypes.byref(bad), ctypes.byref(c), 1, 1, 100, *([None] * 8), None, 0,
                           None) == -2
     assert lib.qsa_status_string(-3) == b"workspace missing, too small or misaligned"
+
+
+def test_append_argument_checks():
+    lib = qsa.load()
+    g = qsa._geom(workload.geometry(kv_dtype="fp8", k_scale=0.5, v_scale=0.5))
+    nul = [None] * 4
+    # null caches / tensors with work to do: refused before any launch
+    assert lib.qsa_append_kv(ctypes.byref(g), *nul, 4, 4, 1, None, None, 3, None, None, None,
+                             None) == -1
+    # nothing to append: success without touching any pointer
+    assert lib.qsa_append_kv(ctypes.byref(g), *nul, 4, 4, 0, None, None, 3, None, None, None,
+                             None) == 0
+    assert lib.qsa_append_kv(ctypes.byref(g), *nul, 4, 4, 2, None, None, 0, None, None, None,
+                             None) == 0
+    assert lib.qsa_append_kv(ctypes.byref(g), *nul, 4, 4, -1, None, None, 3, None, None, None,
+                             None) == -1
+    bad = qsa._geom(dict(workload.geometry(), num_kv_heads=3))
+    assert lib.qsa_append_kv(ctypes.byref(bad), *nul, 4, 4, 1, None, None, 3, None, None, None,
+                             None) == -2
+    assert [qsa.append_khat_slots(n) for n in (-1, 0, 1, 4, 5, 8, 4096)] == [0, 0, 1, 1, 2, 2,
+                                                                           1024]
