@@ -57,8 +57,8 @@ def lib():
         L.qo_bf16.argtypes = [ctypes.c_uint16]
         L.qo_round_bf16.restype = ctypes.c_float
         L.qo_round_bf16.argtypes = [ctypes.c_float]
-        L.qo_scores.argtypes = [i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, i32, i32,
-                                i32, vp]
+        L.qo_scores.argtypes = [i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, i32,
+                                i32, i32, vp]
         L.qo_topk.restype = i32
         L.qo_topk.argtypes = [i32, vp, i32, vp, i32, vp]
         L.qo_expand.restype = i32
@@ -117,8 +117,10 @@ def scores(row_req, row_len, q_idx, w_idx, khat, page_table, num_pages, gstride,
     khat = _c(khat, np.float32)
     page_table = _c(page_table, np.int32)
     n, Hi, Di = q_idx.shape
+    Hk = khat.shape[2]  # key heads of k̂: Hi (per-head form) or 1 (multi-query form)
+    assert khat.shape[3] == Di and Hk >= 1 and Hi % Hk == 0
     out = np.empty((n, gstride), np.float32)
-    lib().qo_scores(n, _p(row_req), _p(row_len), Hi, Di, PAGE, RATIO, _p(q_idx), _p(w_idx),
+    lib().qo_scores(n, _p(row_req), _p(row_len), Hi, Hk, Di, PAGE, RATIO, _p(q_idx), _p(w_idx),
                     _p(khat), _p(page_table), page_table.shape[1], int(num_pages),
                     int(bool(round_bf16_inputs)), int(gstride), _p(out))
     return out

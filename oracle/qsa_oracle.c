@@ -179,10 +179,15 @@ static double kv_value(const void* cache, int kv_dtype, int64_t index) {
 /* Step 1: indexer scores                                                 */
 /* ---------------------------------------------------------------------- */
 
-/* score[g] = sum_h w[h] * max(0, sum_d q[h][d] * khat[g][h][d]) for every
- * complete group g < floor(L/ratio) of the row; -inf for g >= floor(L/ratio)
- * and for groups whose page id is out of range.  The form is the assumed
- * per-head ReLU-weighted indexer (the pages do not print one).
+/* score[g] = sum_h w[h] * max(0, sum_d q[h][d] * khat[g][kh(h)][d]) for
+ * every complete group g < floor(L/ratio) of the row; -inf for
+ * g >= floor(L/ratio) and for groups whose page id is out of range.  The
+ * form is the assumed ReLU-weighted indexer (the pages do not print one).
+ * The k̂ of a group has Hk key heads; query head h reads key head
+ * kh(h) = h * Hk / Hi.  Hk = Hi is the per-head form (8 x 64); Hk = 1 is the
+ * multi-query form of the OrcaRouter article on PR #41855, "Warum QSA der
+ * heikle Teil ist - in Zahlen" (4 query heads sharing 1 key head of
+ * dimension 128).
  * Products of two binary32 values are exact in binary64 and the sums run in
  * binary64, so the single final rounding to binary32 gives (up to a
  * double-rounding tie) the correctly rounded score.  With round_bf16 != 0
@@ -190,7 +195,7 @@ static double kv_value(const void* cache, int kv_dtype, int64_t index) {
  * gstride is the row stride of `out`; columns >= floor(L/ratio) up to
  * gstride are set to -inf.  Rows with L < 0 or floor(L/ratio) > gstride
  * (more complete groups than the row holds) get all -inf. */
-void qo_scores(int n_rows, const int32_t* row_req, const int32_t* row_len, int Hi, int Di,
+void qo_scores(int n_rows, const int32_t* row_req, const int32_t* row_len, int Hi, int Hk, int Di,
                int page, int ratio, const float* q_idx, const float* w_idx, const float* khat,
                const int32_t* page_table, int max_pages, int num_pages, int round_bf16,
                int gstride, float* out) {
@@ -206,12 +211,12 @@ void qo_scores(int n_rows, const int32_t* row_req, const int32_t* row_len, int H
     for (int g = 0; g < G; ++g) {
       int32_t phys = page_table[(int64_t)row_req[r] * max_pages + g / gpp];
       if (!page_ok(phys, num_pages)) continue;
-      const float* kg = khat + ((int64_t)phys * gpp + g % gpp) * Hi * Di;
+      const float* kg = khat + ((int64_t)phys * gpp + g % gpp) * Hk * Di;
       double s = 0.0;
       for (int h = 0; h < Hi; ++h) {
         double a = 0.0;
         for (int d = 0; d < Di; ++d) {
-          float qv = q[h * Di + d], kv = kg[h * Di + d];
+          float qv = q[h * Di + d], kv = kg[(h * Hk / Hi) * Di + d];
           if (round_bf16) { qv = qo_round_bf16(qv); kv = qo_round_bf16(kv); }
           a += (double)qv * (double)kv;
         }

@@ -130,3 +130,48 @@ def test_out_of_range_page_scores_minus_inf():
     s = oracle.scores([0], [4 * G], np.ones((1, Hi, Di), np.float32),
                       np.ones((1, Hi), np.float32), kh, pt, kh.shape[0], G)[0]
     assert np.all(s[:16] == 64 * 8) and np.all(np.isneginf(s[16:]))
+
+
+# --- the multi-query indexer form (OrcaRouter article on PR #41855, "Warum QSA
+# der heikle Teil ist - in Zahlen": 4 query heads share 1 key head, dim 128)
+
+def test_mqa_equals_per_head_form_with_replicated_key():
+    # one shared key head == the per-head form with that key in every head
+    rng = np.random.default_rng(11)
+    Hi, Di, G = 4, 128, 40
+    q = rng.normal(size=(Hi, Di)).astype(np.float32)
+    w = rng.uniform(0, 1, Hi).astype(np.float32)
+    k1 = rng.normal(size=(G, 1, Di)).astype(np.float32)
+    a = run(q, w, k1)
+    b = run(q, w, np.repeat(k1, Hi, axis=1))
+    assert np.array_equal(a, b)
+
+
+def test_mqa_one_hot_key_reads_every_query_head():
+    # k̂_g = e_{j(g)} shared by all heads  =>  s_g = sum_h w_h max(q_h[j(g)], 0)
+    rng = np.random.default_rng(12)
+    Hi, Di, G = 4, 128, 64
+    q = rng.integers(-4, 5, (Hi, Di)).astype(np.float32)
+    w = np.array([0.5, 1.0, 2.0, 4.0], np.float32)
+    j = (np.arange(G) * 37) % Di
+    kg = np.zeros((G, 1, Di), np.float32)
+    kg[np.arange(G), 0, j] = 1.0
+    s = run(q, w, kg)[:G]
+    want = (np.maximum(q[:, j], 0) * w[:, None]).sum(axis=0)   # exact small integers / 2
+    assert np.array_equal(s, want.astype(np.float32))
+
+
+def test_mqa_relu_keeps_only_aligned_heads():
+    # q_h = sign_h * c_h * k (one key for all groups): heads with a negative
+    # sign contribute 0, the others w_h c_h |k|^2
+    rng = np.random.default_rng(13)
+    Di, G = 128, 20
+    k = rng.integers(-2, 3, Di).astype(np.float32)
+    sign = np.array([1, -1, 1, -1], np.float32)
+    c = np.array([1, 2, 3, 4], np.float32)
+    q = (sign * c)[:, None] * k[None, :]
+    w = np.array([1.0, 1.0, 0.25, 1.0], np.float32)
+    kg = np.repeat(k[None, None, :], G, axis=0)
+    s = run(q, w, kg)[:G]
+    n2 = float(k @ k)
+    assert np.all(s == np.float32((1.0 * 1 + 0.25 * 3) * n2))
