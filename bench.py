@@ -230,6 +230,53 @@ def prefill_scoring(dev, steps: int, warmup: int) -> dict:
             "prefill_step_ms": ms_step}
 
 
+def kv_append(dev, steps: int, warmup: int) -> dict:
+    """The cache append of the long-prefill chunk: 4,096 new tokens' K and V
+    (bf16, 2 KV heads x 256) written into an FP8 E4M3 paged cache at
+    positions 28,672 .. 32,767, and the k-hat of the 1,024 groups they
+    complete.  A streaming copy: HBM bytes read + written per call."""
+    import numpy as np
+    import torch
+    import learned_sparse_attention_amd as qsa
+    import workload
+    n, start, hkv, dim = 4096, 28672, 2, 256
+    P = (start + n) // 64
+    g = workload.geometry(kv_dtype="fp8", k_scale=0.02, v_scale=0.02)
+    perm = workload.permutation(0x5A, 1, P)
+    pt = torch.from_numpy(perm.reshape(1, P).astype(np.int32)).to(dev)
+    kc = torch.zeros((P, 64, hkv, dim), dtype=torch.uint8, device=dev)
+    vc = torch.zeros_like(kc)
+    kh = torch.zeros((P, 16, 8, 64), dtype=torch.float32, device=dev)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    kn = t(workload.normal_bf16(0x5A, 2, (1, n, hkv, dim)).view(np.int16))
+    vn = t(workload.normal_bf16(0x5A, 3, (1, n, hkv, dim)).view(np.int16))
+    slots = qsa.append_khat_slots(n)
+    khn = t(workload.normal_f32(0x5A, 4, (1, slots, 8, 64)))
+    rows, sp = t(np.zeros(1, np.int32)), t(np.array([start], np.int32))
+
+    def call():
+        qsa.qsa_append_kv(g, kc, vc, kh, pt, rows, sp, kn, vn, khn, num_pages=P)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    groups = (start + n) // 4 - start // 4
+    nbytes = 2 * n * hkv * dim * (2 + 1) + groups * 8 * 64 * 4 * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "append of 4,096 tokens (positions 28,672..32,767) into an FP8 E4M3 "
+                        "paged cache, 2 KV heads x 256, plus 1,024 k-hat groups",
+            "kernels": ["append_kv_kernel", "append_khat_kernel"], "bound": "hbm",
+            "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "bytes_per_call": nbytes, "ms_per_call": ms}
+
+
 def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
     """The oracle, unchanged, on this host: full decode steps of a bounded
     subset of requests, scaled to layer-steps/s of the whole batch."""
@@ -364,6 +411,7 @@ def main() -> int:
     }
     if not args.no_prefill:
         result["prefill_scoring"] = prefill_scoring(dev, max(5, args.steps // 2), 3)
+        result["kv_append"] = kv_append(dev, max(20, args.steps), 5)
     if args.calibrate_copy:
         calibrate_copy(dev)
     if not args.no_cpu_baseline:

@@ -12,8 +12,10 @@
  *      group of 4 consecutive tokens (compress ratio 4, "C4").  The pages do
  *      not print the indexer formula; this library uses, per query row and
  *      complete group g,
- *          score[g] = sum_h  w[h] * max(0, sum_d q_idx[h,d] * khat[g,h,d])
- *      with H_i = 8 indexer heads of dimension 64 (all fp32 inputs).
+ *          score[g] = sum_h  w[h] * max(0, sum_d q_idx[h,d] * khat[g,kh(h),d])
+ *      with H_i = 8 indexer heads of dimension 64 and a key per head
+ *      (kh(h) = h), or the multi-query form of 4 heads of dimension 128
+ *      sharing one key (kh(h) = 0); all inputs fp32.
  *   2. Exact top-K.  Among the complete groups g < floor(L/4) (L = tokens
  *      including the current one) keep the K = topk_groups highest scores,
  *      ranking by (score descending, group index ascending); K is a group
@@ -75,24 +77,32 @@ enum qsa_kv_dtype {
 };
 
 /* Layer geometry.  The supported values follow the pages' configurations:
- * head_dim 256, page_size 64, compress_ratio 4 (C4), an indexer of 8 heads x
- * 64 dims, a group budget topk_groups in [1, 2048] (the pages use 512, 1024
- * and 2048), and any GQA ratio num_q_heads / num_kv_heads with
- * (num_q_heads / num_kv_heads) * q_per_req <= 64 query rows per KV head. */
+ * head_dim 256, page_size 64, compress_ratio 4 (C4), a group budget
+ * topk_groups in [1, 2048] (the pages use 512, 1024 and 2048), any GQA
+ * ratio num_q_heads / num_kv_heads with (num_q_heads / num_kv_heads) *
+ * q_per_req <= 64 query rows per KV head, and one of two indexer forms:
+ *   - per head: idx_heads 8, idx_dim 64, idx_key_heads 8 (or 0), a key of
+ *     8 x 64 fp32 per group (2 KiB);
+ *   - multi-query (OrcaRouter article on PR #41855, "Warum QSA der heikle
+ *     Teil ist - in Zahlen": 4 query heads share 1 key head of dimension
+ *     128): idx_heads 4, idx_dim 128, idx_key_heads 1, a key of 128 fp32
+ *     per group (512 B).  Query head h reads key head
+ *     h * idx_key_heads / idx_heads. */
 typedef struct qsa_geometry {
   int32_t num_q_heads;    /* Hq, e.g. 16 or 24 */
   int32_t num_kv_heads;   /* Hkv, e.g. 2; must divide num_q_heads */
   int32_t head_dim;       /* D = 256 */
   int32_t page_size;      /* tokens per KV page = 64 */
   int32_t compress_ratio; /* tokens per indexer group = 4 */
-  int32_t idx_heads;      /* H_i = 8 */
-  int32_t idx_dim;        /* D_i = 64 */
+  int32_t idx_heads;      /* H_i = 8 (per-head form) or 4 (multi-query form) */
+  int32_t idx_dim;        /* D_i = 64 or 128 */
   int32_t topk_groups;    /* K, group budget, 1..2048 */
   int32_t kv_dtype;       /* enum qsa_kv_dtype */
   float sm_scale;         /* softmax scale; <= 0 selects 1/sqrt(head_dim) */
   float k_scale;          /* K element = decoded code * k_scale (FP8 per-tensor
                              dequant factor; 1 for unscaled BF16) */
   float v_scale;          /* V element = decoded code * v_scale */
+  int32_t idx_key_heads;  /* H_k: indexer key heads per group, 8 or 1 (0 = H_i) */
 } qsa_geometry;
 
 /* The paged caches of one attention layer.  Logical token t of the request
@@ -108,7 +118,7 @@ typedef struct qsa_geometry {
 typedef struct qsa_paged_cache {
   const void* k;              /* [num_pages, page_size, Hkv, D] bf16 or fp8 */
   const void* v;              /* [num_pages, page_size, Hkv, D] bf16 or fp8 */
-  const float* khat;          /* [num_pages, page_size/ratio, H_i, D_i] f32 */
+  const float* khat;          /* [num_pages, page_size/ratio, H_k, D_i] f32 */
   const int32_t* page_table;  /* [rows, max_pages] int32 */
   int32_t max_pages;          /* row stride of page_table (host) */
   int32_t num_pages;          /* physical pages in k, v and khat (host) */
@@ -283,7 +293,7 @@ int32_t qsa_append_khat_slots(int32_t n_tokens);
  *             nearest bfloat16 (ties to even) for a BF16 cache, which is x
  *             itself when the scale is 1.  The pages print no quantiser;
  *             this is the library's reading.
- *   khat_new  nullable [n_req, qsa_append_khat_slots(n_tokens), H_i, D_i]
+ *   khat_new  nullable [n_req, qsa_append_khat_slots(n_tokens), H_k, D_i]
  *             f32.  Slot j of request r holds group
  *             g = floor(start_pos[r] / 4) + j.  It is written (copied) when
  *             that group's last token 4g + 3 is among the new tokens.

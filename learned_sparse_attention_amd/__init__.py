@@ -39,7 +39,8 @@ class Geometry(ctypes.Structure):
                 ("compress_ratio", ctypes.c_int32), ("idx_heads", ctypes.c_int32),
                 ("idx_dim", ctypes.c_int32), ("topk_groups", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float),
-                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+                ("idx_key_heads", ctypes.c_int32)]
 
 
 class PagedCache(ctypes.Structure):
@@ -93,6 +94,8 @@ def load():
 
 
 def _geom(g: dict) -> Geometry:
+    g = dict(g)
+    g.setdefault("idx_key_heads", g["idx_heads"])  # per-head form unless stated
     return Geometry(*(int(g[f]) if t is ctypes.c_int32 else float(g[f])
                       for f, t in Geometry._fields_))
 

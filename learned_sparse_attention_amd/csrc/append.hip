@@ -58,6 +58,7 @@ struct AppendArgs {
   const uint16_t* v_new;
   const float* khat_new;
   int khat_slots;
+  int group_f4;   // float4 per k̂ group: 128 (8 heads x 64) or 32 (one key of 128)
   int row_elems;  // Hkv * D
   float k_scale, v_scale;
 };
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(256) void append_kv_kernel(AppendArgs a) {
 }
 
 __global__ __launch_bounds__(256) void append_khat_kernel(AppendArgs a) {
-  constexpr int kF4 = kGroupFloats / 4;  // float4 per group
+  const int kF4 = a.group_f4;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long long)a.n_req * a.khat_slots * kF4) return;
   const long long slot = idx / kF4;  // request r, slot j
@@ -126,9 +127,9 @@ __global__ __launch_bounds__(256) void append_khat_kernel(AppendArgs a) {
   if (g / kGroupsPerPage >= a.max_pages) return;
   const int32_t p = a.page_table[(long long)a.req_rows[r] * a.max_pages + g / kGroupsPerPage];
   if (p < 0 || p >= a.num_pages) return;
-  const float4 v = stream_load(reinterpret_cast<const float4*>(a.khat_new + slot * kGroupFloats) + f);
-  reinterpret_cast<float4*>(a.khat_cache + ((long long)p * kGroupsPerPage + g % kGroupsPerPage) *
-                                               kGroupFloats)[f] = v;
+  const float4 v = stream_load(reinterpret_cast<const float4*>(a.khat_new) + slot * kF4 + f);
+  reinterpret_cast<float4*>(a.khat_cache)[((long long)p * kGroupsPerPage + g % kGroupsPerPage) *
+                                              kF4 + f] = v;
 }
 
 }  // namespace
@@ -137,12 +138,12 @@ hipError_t launch_append(void* k_cache, void* v_cache, float* khat_cache,
                          const int32_t* page_table, int max_pages, int num_pages, int n_req,
                          const int32_t* req_rows, const int32_t* start_pos, int n_tokens,
                          const uint16_t* k_new, const uint16_t* v_new, const float* khat_new,
-                         int row_elems, int kv_dtype, float k_scale, float v_scale,
-                         hipStream_t stream) {
+                         int khat_group_floats, int row_elems, int kv_dtype, float k_scale,
+                         float v_scale, hipStream_t stream) {
   if (n_req <= 0 || n_tokens <= 0) return hipSuccess;
   AppendArgs a{k_cache, v_cache, khat_cache, page_table, max_pages, num_pages, n_req, n_tokens,
                req_rows, start_pos, k_new, v_new, khat_new, (n_tokens + kRatio - 1) / kRatio,
-               row_elems, k_scale, v_scale};
+               khat_group_floats / 4, row_elems, k_scale, v_scale};
   const long long n_kv = (long long)n_req * n_tokens * (row_elems / 8);
   const int blocks_kv = (int)((n_kv + 255) / 256);
   if (kv_dtype == 1)
@@ -150,7 +151,7 @@ hipError_t launch_append(void* k_cache, void* v_cache, float* khat_cache,
   else
     hipLaunchKernelGGL(append_kv_kernel<false>, dim3(blocks_kv), dim3(256), 0, stream, a);
   if (khat_new) {
-    const long long n_kh = (long long)n_req * a.khat_slots * (kGroupFloats / 4);
+    const long long n_kh = (long long)n_req * a.khat_slots * a.group_f4;
     hipLaunchKernelGGL(append_khat_kernel, dim3((int)((n_kh + 255) / 256)), dim3(256), 0, stream,
                        a);
   }

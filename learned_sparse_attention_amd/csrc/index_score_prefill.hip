@@ -42,21 +42,39 @@ constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfQueries = 32 * kPfWaves;  // queries per workgroup
 constexpr int kPfGroups = 32;              // groups per block
-constexpr int kPfKSteps = kIdxDim / 16;    // 4 MFMA k-steps per head
 // LDS slots are 16 bytes (8 bf16, one MFMA operand per lane).  A k̂ block
-// is [head][k-step][half] rows of 32 group slots; q staging is rows of 256
-// query slots.  Each row is padded by one slot, so that the 32 rows a
+// is [key head][k-step][half] rows of 32 group slots; q staging is rows of
+// 256 query slots.  Each row is padded by one slot, so that the 32 rows a
 // wavefront writes at once (one group or query, all heads) start in
 // different LDS banks.
 constexpr int kKPitch = kPfGroups + 1;
 constexpr int kQPitch = kPfQueries + 1;
-constexpr int kKRows = kIdxHeads * kPfKSteps * 2;   // 64
-constexpr int kKBlockSlots = kKRows * kKPitch;      // 2,112 slots = 33 KiB
-constexpr int kQRounds = 2;                         // q staged 4 heads at a time
-constexpr int kQRoundHeads = kIdxHeads / kQRounds;
-constexpr int kQSlots = kQRoundHeads * kPfKSteps * 2 * kQPitch;  // 8,224 slots = 128.5 KiB
-constexpr int kLdsSlots = kQSlots > 2 * kKBlockSlots ? kQSlots : 2 * kKBlockSlots;
 constexpr int kXcds = 8;
+
+// Indexer forms: kH query heads of kD dims per query row; each group's k̂
+// holds kHk key heads, query head h reading key head h * kHk / kH.
+//   - per-head form: 8 heads x 64 dims, one key per head (2 KiB per group);
+//   - multi-query form (OrcaRouter article on PR #41855, "Warum QSA der
+//     heikle Teil ist - in Zahlen"): 4 heads x 128 dims sharing one key
+//     head (512 B per group).
+template <int H, int Hk, int D>
+struct Form {
+  static constexpr int kH = H, kHk = Hk, kD = D;
+  static constexpr int kS = D / 16;           // MFMA k-steps per head
+  static constexpr int kGF = Hk * D;          // fp32 per group of k̂
+  static constexpr int kQF = H * D;           // fp32 per query row
+  static constexpr int kKBlockSlots = Hk * kS * 2 * kKPitch;
+  static constexpr int kQRoundHeads = 16 / kS;  // 256 fp32 of a query row per staging round
+  static constexpr int kQRounds = H / kQRoundHeads;
+  static constexpr int kQSlots = kQRoundHeads * kS * 2 * kQPitch;  // 8,224 slots = 128.5 KiB
+  static constexpr int kLdsSlots = kQSlots > 2 * kKBlockSlots ? kQSlots : 2 * kKBlockSlots;
+  static constexpr int kPagesF4 = kGroupsPerPage * kGF / 4;  // float4 per k̂ page
+  static constexpr int kFetch = 2 * kPagesF4 / kPfThreads;    // float4 per thread per block
+  static_assert(kQRoundHeads * D == 256 && H % kQRoundHeads == 0 && H % Hk == 0, "form");
+  static_assert(kFetch >= 1 && (kPagesF4 & (kPagesF4 - 1)) == 0, "form");
+};
+using PerHeadForm = Form<kIdxHeads, kIdxHeads, kIdxDim>;
+using SharedKeyForm = Form<4, 1, 128>;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -80,13 +98,16 @@ __device__ __forceinline__ u32x4 pack8_bf16(float4 a, float4 b) {
                  __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
 }
 
+template <class F>
 __global__ __launch_bounds__(kPfThreads, 1) void index_score_mfma_kernel(
     const float* __restrict__ khat, const int32_t* __restrict__ page_table, int max_pages,
     int num_pages, int req, int first_pos, int n_q, const float* __restrict__ q_idx,
     const float* __restrict__ w_idx, float* __restrict__ scores, int gstride, int n_qt,
     int blocks_per_sweep) {
   // two k̂ block buffers; at the start the same memory stages q
-  __shared__ u32x4 lds[kLdsSlots];
+  constexpr int kH = F::kH, kS = F::kS, kD = F::kD, kQRoundHeads = F::kQRoundHeads;
+  constexpr int kKBlockSlots = F::kKBlockSlots;
+  __shared__ u32x4 lds[F::kLdsSlots];
 
   // workgroup -> (query tile, sweep).  Workgroups are dealt to the XCDs
   // round-robin, so linear id lin = (b % 8) * (nb / 8) + b / 8 gives each
@@ -123,40 +144,41 @@ __global__ __launch_bounds__(kPfThreads, 1) void index_score_mfma_kernel(
   // then every lane picks up its own query's 16 operands.  Rows past the
   // chunk repeat the last row: a query column only feeds its own scores,
   // which are not stored.
-  u32x4 qb[kIdxHeads][kPfKSteps];
-  float wv[kIdxHeads];
+  u32x4 qb[kH][kS];
+  float wv[kH];
   {
     const int qr = min(qi, n_q - 1);
 #pragma unroll
-    for (int h = 0; h < kIdxHeads; ++h) wv[h] = w_idx[(size_t)qr * kIdxHeads + h];
+    for (int h = 0; h < kH; ++h) wv[h] = w_idx[(size_t)qr * kH + h];
     u32x2* lds8 = reinterpret_cast<u32x2*>(lds);
 #pragma unroll
-    for (int rd = 0; rd < kQRounds; ++rd) {
-      constexpr int kPer = kPfQueries * kQRoundHeads * (kIdxDim / 4) / kPfThreads;  // 32 float4
+    for (int rd = 0; rd < F::kQRounds; ++rd) {
+      constexpr int kPer = kPfQueries * kQRoundHeads * (kD / 4) / kPfThreads;  // 32 float4
       float4 x[kPer];
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const int f = i * kPfThreads + tid;
-        const int r = f >> 6, c = f & 63;  // row, float4 within the round's 4 heads
+        const int r = f >> 6, c = f & 63;  // row, float4 within the round's heads
         const int row = min(qt * kPfQueries + r, n_q - 1);
-        x[i] = reinterpret_cast<const float4*>(q_idx + (size_t)row * kGroupFloats +
-                                               rd * kQRoundHeads * kIdxDim)[c];
+        x[i] = reinterpret_cast<const float4*>(q_idx + (size_t)row * F::kQF +
+                                               rd * kQRoundHeads * kD)[c];
       }
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const int f = i * kPfThreads + tid;
         const int r = f >> 6, c = f & 63;
-        const int hh = c >> 4, m = c & 15, cc = m >> 1;  // dims 4m.. = chunk cc, half m & 1
-        const int slot = ((hh * kPfKSteps + (cc & 3)) * 2 + (cc >> 2)) * kQPitch + r;
+        // dims 4m.. of head hh = chunk cc (k-step cc % kS, lane half cc / kS)
+        const int hh = c / (kD / 4), m = c % (kD / 4), cc = m >> 1;
+        const int slot = ((hh * kS + cc % kS) * 2 + cc / kS) * kQPitch + r;
         lds8[2 * slot + (m & 1)] = pack4_bf16(x[i]);
       }
       __syncthreads();
 #pragma unroll
       for (int hh = 0; hh < kQRoundHeads; ++hh)
 #pragma unroll
-        for (int s = 0; s < kPfKSteps; ++s)
+        for (int s = 0; s < kS; ++s)
           qb[rd * kQRoundHeads + hh][s] =
-              lds[((hh * kPfKSteps + s) * 2 + hf) * kQPitch + wave * 32 + ql];
+              lds[((hh * kS + s) * 2 + hf) * kQPitch + wave * 32 + ql];
       __syncthreads();
     }
   }
@@ -176,8 +198,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void index_score_mfma_kernel(
     return r;
   };
   auto page_valid = [&](int p) { return p >= 0 && p < num_pages; };
-  constexpr int kPagesF4 = kGroupsPerPage * kGroupFloats / 4;  // 2,048 float4 per page
-  constexpr int kFetch = 2 * kPagesF4 / kPfThreads;             // 8 float4 per thread
+  constexpr int kPagesF4 = F::kPagesF4;  // 2,048 (per-head form) or 512 float4 per page
+  constexpr int kFetch = F::kFetch;      // 8 or 2 float4 per thread
   float4 pre[kFetch];
   // A page that is out of range (or past the row) is read as page 0
   // instead, always a valid address: its groups' k̂ feed only their own
@@ -200,9 +222,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void index_score_mfma_kernel(
     for (int i = 0; i < kFetch; ++i) {
       const int f = i * kPfThreads + tid;
       const int e = f & (kPagesF4 - 1);
-      const int g = (f >> 11) * kGroupsPerPage + (e >> 7);  // group within the block
-      const int col = e & 127, h = col >> 4, m = col & 15, cc = m >> 1;
-      const int slot = ((h * kPfKSteps + (cc & 3)) * 2 + (cc >> 2)) * kKPitch + g;
+      const int g = (f / kPagesF4) * kGroupsPerPage + e / (F::kGF / 4);  // group within the block
+      const int col = e % (F::kGF / 4), kh = col / (kD / 4), m = col % (kD / 4), cc = m >> 1;
+      const int slot = ((kh * kS + cc % kS) * 2 + cc / kS) * kKPitch + g;
       kl8[2 * slot + (m & 1)] = pack4_bf16(pre[i]);
     }
   };
@@ -271,8 +293,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void index_score_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
 #pragma unroll
-        for (int s = 0; s < kPfKSteps; ++s) {
-          const u32x4 a = kb[(h * kPfKSteps + s) * 2 * kKPitch];
+        for (int s = 0; s < kS; ++s) {
+          const u32x4 a = kb[((h * F::kHk / kH) * kS + s) * 2 * kKPitch];
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                         __builtin_bit_cast(bf16x8, qb[h][s]), acc,
                                                         0, 0, 0);
@@ -281,14 +303,14 @@ __global__ __launch_bounds__(kPfThreads, 1) void index_score_mfma_kernel(
       };
       f32x16 prev = head(0);
 #pragma unroll
-      for (int h = 1; h <= kIdxHeads; ++h) {
+      for (int h = 1; h <= kH; ++h) {
         f32x16 cur;
-        if (h < kIdxHeads) cur = head(h);
+        if (h < kH) cur = head(h);
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           sc[i] += wv[h - 1] * __int_as_float(max(__float_as_int(prev[i]), 0));
         __builtin_amdgcn_sched_barrier(0);
-        if (h < kIdxHeads) prev = cur;
+        if (h < kH) prev = cur;
       }
     }
     if (more) stash(buf ^ 1);
@@ -325,7 +347,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void index_score_mfma_kernel(
 hipError_t launch_index_score_prefill(const float* khat, const int32_t* page_table,
                                       int max_pages, int num_pages, int req, int first_pos,
                                       int n_q, const float* q_idx, const float* w_idx,
-                                      float* scores, int gstride, hipStream_t stream) {
+                                      float* scores, int gstride, hipStream_t stream,
+                                      bool shared_key) {
   if (n_q <= 0 || gstride <= 0) return hipSuccess;
   const int n_qt = (n_q + kPfQueries - 1) / kPfQueries;
   const int n_gb = (gstride + kPfGroups - 1) / kPfGroups;
@@ -335,7 +358,9 @@ hipError_t launch_index_score_prefill(const float* khat, const int32_t* page_tab
   const int bps = (n_gb + sweeps - 1) / sweeps;
   sweeps = (n_gb + bps - 1) / bps;
   const int grid = n_qt * sweeps;
-  hipLaunchKernelGGL(index_score_mfma_kernel, dim3(grid), dim3(kPfThreads), 0, stream, khat,
+  auto kern = shared_key ? index_score_mfma_kernel<SharedKeyForm>
+                        : index_score_mfma_kernel<PerHeadForm>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kPfThreads), 0, stream, khat,
                      page_table, max_pages, num_pages, req, first_pos, n_q, q_idx, w_idx, scores,
                      gstride, n_qt, bps);
   return hipGetLastError();

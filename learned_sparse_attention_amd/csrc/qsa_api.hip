@@ -22,6 +22,9 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int gstride_of(int max_ctx) { return max_ctx / kRatio; }
 
+// multi-query indexer form (4 heads x 128, one shared key head per group)
+bool shared_key(const qsa_geometry* g) { return g->idx_key_heads == 1; }
+
 // Decode attention: selection entries per split-K workgroup.  Aims at
 // roughly 512 workgroups over the whole batch, with at least 16 groups (64
 // tokens, one 16-token sub-tile per wavefront) per workgroup.
@@ -139,9 +142,14 @@ const char* qsa_status_string(qsa_status s) {
 
 qsa_status qsa_validate(const qsa_geometry* g) {
   if (!g) return QSA_ERR_INVALID_ARG;
-  if (g->head_dim != kHeadDim || g->page_size != kPage || g->compress_ratio != kRatio ||
-      g->idx_heads != kIdxHeads || g->idx_dim != kIdxDim)
+  if (g->head_dim != kHeadDim || g->page_size != kPage || g->compress_ratio != kRatio)
     return QSA_ERR_UNSUPPORTED;
+  // the two indexer forms: 8 heads x 64 with a key per head (idx_key_heads
+  // 8, or 0), or 4 heads x 128 sharing one key head
+  const bool per_head = g->idx_heads == kIdxHeads && g->idx_dim == kIdxDim &&
+                        (g->idx_key_heads == kIdxHeads || g->idx_key_heads == 0);
+  const bool shared = g->idx_heads == 4 && g->idx_dim == 128 && g->idx_key_heads == 1;
+  if (!per_head && !shared) return QSA_ERR_UNSUPPORTED;
   if (g->topk_groups < 1 || g->topk_groups > 2048) return QSA_ERR_UNSUPPORTED;
   if (g->num_kv_heads < 1 || g->num_q_heads < g->num_kv_heads ||
       g->num_q_heads % g->num_kv_heads != 0 || g->num_q_heads / g->num_kv_heads > 16)
@@ -190,7 +198,7 @@ qsa_status qsa_index_score(const qsa_geometry* g, const qsa_paged_cache* cache, 
   QSA_HIP(launch_index_score_gemv(cache->khat, cache->page_table, cache->max_pages,
                                   cache->num_pages, n_rows, row_req, row_len, 0, 0, max_ctx,
                                   q_idx, w_idx, out_scores, gstride_of(max_ctx),
-                                  (hipStream_t)stream));
+                                  (hipStream_t)stream, nullptr, shared_key(g)));
   return QSA_OK;
 }
 
@@ -206,7 +214,8 @@ qsa_status qsa_index_score_prefill(const qsa_geometry* g, const qsa_paged_cache*
   if (!q_idx || !w_idx || !out_scores) return QSA_ERR_INVALID_ARG;
   QSA_HIP(launch_index_score_prefill(cache->khat, cache->page_table, cache->max_pages,
                                      cache->num_pages, req, first_pos, n_q, q_idx, w_idx,
-                                     out_scores, gstride_of((int)total), (hipStream_t)stream));
+                                     out_scores, gstride_of((int)total), (hipStream_t)stream,
+                                     shared_key(g)));
   return QSA_OK;
 }
 
@@ -228,7 +237,7 @@ qsa_status qsa_index_topk(const qsa_geometry* g, const qsa_paged_cache* cache, i
   float* samples = (float*)((char*)ws + lay.off_samples);
   QSA_HIP(launch_index_score_gemv(cache->khat, cache->page_table, cache->max_pages,
                                   cache->num_pages, n_rows, row_req, row_len, 0, 0, max_ctx,
-                                  q_idx, w_idx, scores, lay.gstride, s, samples));
+                                  q_idx, w_idx, scores, lay.gstride, s, samples, shared_key(g)));
   QSA_HIP(launch_topk(scores, lay.gstride, n_rows, row_len, 0, max_ctx, g->topk_groups,
                       out_groups, (char*)ws + lay.off_topk, s, samples));
   return QSA_OK;
@@ -259,7 +268,7 @@ qsa_status qsa_decode(const qsa_geometry* g, const qsa_paged_cache* cache, int32
   QSA_HIP(launch_index_score_gemv(cache->khat, cache->page_table, cache->max_pages,
                                   cache->num_pages, batch, nullptr, ctx_lens, 0, 0,
                                   max_ctx - (q_per_req - 1), q_idx, w_idx, scores, lay.gstride, s,
-                                  samples));
+                                  samples, shared_key(g)));
   QSA_HIP(launch_topk(scores, lay.gstride, batch, ctx_lens, 0, max_ctx - (q_per_req - 1),
                       g->topk_groups, sel, w + lay.off_topk, s, samples));
   AttnArgs a = attn_args(g, cache);
@@ -300,7 +309,7 @@ qsa_status qsa_prefill(const qsa_geometry* g, const qsa_paged_cache* cache, int3
   int32_t* sel = out_groups ? out_groups : (int32_t*)(w + lay.off_sel);
   QSA_HIP(launch_index_score_prefill(cache->khat, cache->page_table, cache->max_pages,
                                      cache->num_pages, req, first_pos, n_q, q_idx, w_idx, scores,
-                                     lay.gstride, s));
+                                     lay.gstride, s, shared_key(g)));
   QSA_HIP(launch_topk(scores, lay.gstride, n_q, nullptr, first_pos, max_ctx, g->topk_groups, sel,
                       w + lay.off_topk, s));
   AttnArgs a = attn_args(g, cache);
@@ -338,6 +347,7 @@ qsa_status qsa_append_kv(const qsa_geometry* g, void* k_cache, void* v_cache, fl
   if (!(g->k_scale > 0.0f) || !(g->v_scale > 0.0f)) return QSA_ERR_INVALID_ARG;
   QSA_HIP(launch_append(k_cache, v_cache, khat_cache, page_table, max_pages, num_pages, n_req,
                         req_rows, start_pos, n_tokens, k_new, v_new, khat_new,
+                        (shared_key(g) ? 1 : g->idx_heads) * g->idx_dim,
                         g->num_kv_heads * g->head_dim, g->kv_dtype, g->k_scale, g->v_scale,
                         (hipStream_t)stream));
   return QSA_OK;

@@ -8,7 +8,8 @@
 namespace qsa {
 
 // Indexer scores of `n_rows` query rows over their request's paged k̂
-// (fp32 GEMV).  scores is [n_rows, gstride]; columns g >= floor(L/4) get
+// (fp32 GEMV); shared_key selects the multi-query form (4 heads x 128
+// sharing one key head, 512 B of k̂ per group) over the per-head form.  scores is [n_rows, gstride]; columns g >= floor(L/4) get
 // -inf.  Rows take (request, L) from row_req/row_len; with row_req null,
 // row r uses page-table row r; with both null, rows are queries
 // first_pos + row of request req0.  If samples is non-null and a row has
@@ -20,14 +21,18 @@ hipError_t launch_index_score_gemv(const float* khat, const int32_t* page_table,
                                    int num_pages, int n_rows, const int32_t* row_req,
                                    const int32_t* row_len, int req0, int first_pos, int max_ctx,
                                    const float* q_idx, const float* w_idx, float* scores,
-                                   int gstride, hipStream_t stream, float* samples = nullptr);
+                                   int gstride, hipStream_t stream, float* samples = nullptr,
+                                   bool shared_key = false);
 
 // Indexer scores of a prefill chunk on the matrix cores (bf16 operands,
 // fp32 accumulation): query i of the chunk has L = first_pos + i + 1.
+// shared_key: the multi-query indexer (4 heads x 128 sharing one key head)
+// instead of the per-head form (8 heads x 64).
 hipError_t launch_index_score_prefill(const float* khat, const int32_t* page_table,
                                       int max_pages, int num_pages, int req, int first_pos,
                                       int n_q, const float* q_idx, const float* w_idx,
-                                      float* scores, int gstride, hipStream_t stream);
+                                      float* scores, int gstride, hipStream_t stream,
+                                      bool shared_key = false);
 
 // Exact top-K of each row: candidates g < G(row) where G = floor(L/4) for
 // L = row_len[row] in [0, max_ctx] (else G = 0); when row_len is null,
@@ -73,8 +78,8 @@ hipError_t launch_append(void* k_cache, void* v_cache, float* khat_cache,
                          const int32_t* page_table, int max_pages, int num_pages, int n_req,
                          const int32_t* req_rows, const int32_t* start_pos, int n_tokens,
                          const uint16_t* k_new, const uint16_t* v_new, const float* khat_new,
-                         int row_elems, int kv_dtype, float k_scale, float v_scale,
-                         hipStream_t stream);
+                         int khat_group_floats, int row_elems, int kv_dtype, float k_scale,
+                         float v_scale, hipStream_t stream);
 
 // Expanded token lists: [rows, q_per_req, width], ascending, -1 padded.
 hipError_t launch_expand_tokens(const int32_t* sel, int K, int n_rows, int q_per_req,

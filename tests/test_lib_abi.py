@@ -37,6 +37,11 @@ def test_validate_and_sizes():
                        ("idx_heads", 4), ("idx_dim", 128), ("topk_groups", 4096),
                        ("topk_groups", 0), ("kv_dtype", 7), ("num_kv_heads", 3)):
         assert qsa.validate(dict(g, **{field: bad})) == -2, field
+    # indexer forms: 8 x 64 with a key per head, or 4 x 128 sharing one key
+    assert qsa.validate(dict(g, idx_key_heads=0)) == 0
+    assert qsa.validate(workload.geometry(indexer="mqa")) == 0
+    for hi, di, hk in ((4, 128, 4), (8, 64, 1), (4, 64, 1), (8, 128, 1)):
+        assert qsa.validate(dict(g, idx_heads=hi, idx_dim=di, idx_key_heads=hk)) == -2
     assert qsa.validate(dict(g, k_scale=0.0)) == -1
     assert qsa.validate(dict(g, v_scale=float("nan"))) == -1
     assert qsa.token_width(g, 1) == 4 * 512 + 3

@@ -36,6 +36,9 @@ T_QIDX, T_WIDX, T_Q, T_K, T_V, T_KHAT, T_PAGES, T_LENS = 1, 2, 3, 4, 5, 6, 7, 8
 PAGE = 64
 RATIO = 4
 HI, DI = 8, 64
+# indexer forms: (query heads, key heads, dims) -- a key per head, or one
+# key head shared by 4 query heads of 128 dims (multi-query form)
+INDEXER = {"per_head": (8, 8, 64), "mqa": (4, 1, 128)}
 HEAD_DIM = 256
 CAPACITY = 262_144  # tokens per request (qsa-hisparse offload contract)
 
@@ -168,11 +171,13 @@ class Workload:
 
 
 def geometry(num_q_heads=16, num_kv_heads=2, topk_groups=512, kv_dtype="bf16",
-             sm_scale=0.0, k_scale=1.0, v_scale=1.0) -> dict:
+             sm_scale=0.0, k_scale=1.0, v_scale=1.0, indexer="per_head") -> dict:
+    hi, hk, di = INDEXER[indexer]
     return dict(num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=HEAD_DIM,
-                page_size=PAGE, compress_ratio=RATIO, idx_heads=HI, idx_dim=DI,
+                page_size=PAGE, compress_ratio=RATIO, idx_heads=hi, idx_dim=di,
                 topk_groups=topk_groups, kv_dtype=0 if kv_dtype == "bf16" else 1,
-                sm_scale=float(sm_scale), k_scale=float(k_scale), v_scale=float(v_scale))
+                sm_scale=float(sm_scale), k_scale=float(k_scale), v_scale=float(v_scale),
+                idx_key_heads=hk)
 
 
 def _paged_pool(seed: int, stored: np.ndarray, random_pages: bool, max_pages: int | None = None):
@@ -212,29 +217,32 @@ def _caches(seed, geom, stored, pt, num_pages, idx_bf16_exact):
     (kc, ks), (vc, vs) = caches
     geom = dict(geom, k_scale=ks, v_scale=vs)
     gpp = PAGE // RATIO
-    khat = np.zeros((num_pages, gpp, HI, DI), np.float32)
+    hk, di = geom["idx_key_heads"], geom["idx_dim"]
+    khat = np.zeros((num_pages, gpp, hk, di), np.float32)
     n_groups = np.ascontiguousarray(stored32 // RATIO, np.int32)
-    L.wl_fill_khat_cache(key(seed, T_KHAT), B, _p(n_groups), _p(pt), pt.shape[1], gpp, HI, DI,
+    L.wl_fill_khat_cache(key(seed, T_KHAT), B, _p(n_groups), _p(pt), pt.shape[1], gpp, hk, di,
                          int(idx_bf16_exact), _p(khat))
     return geom, kc, vc, khat
 
 
 def decode_workload(seed: int, ctx_lens, q_per_req=1, num_q_heads=16, num_kv_heads=2,
                     topk_groups=512, kv_dtype="bf16", random_pages=True, sm_scale=0.0,
-                    max_ctx: int | None = None, note="") -> Workload:
+                    max_ctx: int | None = None, note="", indexer="per_head") -> Workload:
     """Decode step: request b has L0 = ctx_lens[b] (base position), its
     cache holds L0 + q_per_req - 1 tokens (the draft positions' KV is
     already written)."""
     ctx = np.ascontiguousarray(np.asarray(ctx_lens, np.int32))
     B = len(ctx)
     stored = ctx + (q_per_req - 1)
-    geom = geometry(num_q_heads, num_kv_heads, topk_groups, kv_dtype, sm_scale)
+    geom = geometry(num_q_heads, num_kv_heads, topk_groups, kv_dtype, sm_scale,
+                    indexer=indexer)
+    hi, di = geom["idx_heads"], geom["idx_dim"]
     mc = int(max_ctx) if max_ctx is not None else int(stored.max())
     mc = max(RATIO, ((mc + RATIO - 1) // RATIO) * RATIO)
     pt, P = _paged_pool(seed, stored, random_pages, max_pages=(mc + PAGE - 1) // PAGE)
     geom, kc, vc, khat = _caches(seed, geom, stored, pt, P, idx_bf16_exact=False)
-    q_idx = normal_f32(seed, T_QIDX, (B, HI, DI))
-    w_idx = uniform_f32(seed, T_WIDX, (B, HI))
+    q_idx = normal_f32(seed, T_QIDX, (B, hi, di))
+    w_idx = uniform_f32(seed, T_WIDX, (B, hi))
     q = normal_bf16(seed, T_Q, (B, q_per_req, num_q_heads, HEAD_DIM))
     return Workload("decode", seed, geom, B, q_per_req, ctx, stored, mc, pt, P, kc, vc, khat,
                     q_idx, w_idx, q, np.arange(B, dtype=np.int32), ctx.copy(), note=note)
@@ -242,17 +250,19 @@ def decode_workload(seed: int, ctx_lens, q_per_req=1, num_q_heads=16, num_kv_hea
 
 def prefill_workload(seed: int, first_pos: int, n_q: int, num_q_heads=16, num_kv_heads=2,
                      topk_groups=512, kv_dtype="bf16", random_pages=True, sm_scale=0.0,
-                     idx_bf16_exact=True, note="") -> Workload:
+                     idx_bf16_exact=True, note="", indexer="per_head") -> Workload:
     """Chunked prefill of one request: queries at positions first_pos ..
     first_pos + n_q - 1 over a cache holding first_pos + n_q tokens."""
     total = first_pos + n_q
     stored = np.array([total], np.int32)
-    geom = geometry(num_q_heads, num_kv_heads, topk_groups, kv_dtype, sm_scale)
+    geom = geometry(num_q_heads, num_kv_heads, topk_groups, kv_dtype, sm_scale,
+                    indexer=indexer)
+    hi, di = geom["idx_heads"], geom["idx_dim"]
     mc = ((total + RATIO - 1) // RATIO) * RATIO
     pt, P = _paged_pool(seed, stored, random_pages, max_pages=(mc + PAGE - 1) // PAGE)
     geom, kc, vc, khat = _caches(seed, geom, stored, pt, P, idx_bf16_exact=idx_bf16_exact)
-    q_idx = normal_f32(seed, T_QIDX, (n_q, HI, DI), bf16_exact=idx_bf16_exact)
-    w_idx = uniform_f32(seed, T_WIDX, (n_q, HI))
+    q_idx = normal_f32(seed, T_QIDX, (n_q, hi, di), bf16_exact=idx_bf16_exact)
+    w_idx = uniform_f32(seed, T_WIDX, (n_q, hi))
     q = normal_bf16(seed, T_Q, (n_q, num_q_heads, HEAD_DIM))
     row_len = np.arange(first_pos + 1, first_pos + n_q + 1, dtype=np.int32)
     return Workload("prefill", seed, geom, 1, 1, np.array([total], np.int32), stored, mc, pt, P,
