@@ -9,8 +9,10 @@ Inputs are seeded and synthetic and resident in HBM before timing.
 Prints one JSON line: layer-steps/s, the roofline position of the dominant
 kernel (the indexer GEMV, HBM-bound) measured with HIP events on the stream
 it runs on, the prefill indexer scoring on the matrix cores against the BF16
-MFMA peak (the long-prefill chunk), and the CPU oracle timed on this host as
-a reported baseline.
+MFMA peak (the long-prefill chunk), the cache append of that chunk against
+the HBM peak, the multi-query indexer form (decode at the Flash-Next shape
+and prefill scoring), and the CPU oracle timed on this host as a reported
+baseline.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
 """
@@ -55,16 +57,18 @@ def algorithmic_bytes(wl) -> dict:
     kv_row = 2 * g["num_kv_heads"] * g["head_dim"] * esize  # K + V of one token
     Q = wl.q_per_req
     khat = scores = pt = pt_score = kv = 0
+    hk = g.get("idx_key_heads", g["idx_heads"])
+    group_bytes = hk * g["idx_dim"] * 4             # fp32 k̂ of one group (2 KiB or 512 B)
     for L in wl.ctx_lens.tolist():
         G = L // 4
-        khat += G * 8 * 64 * 4                    # one 2 KiB fp32 k̂ per complete group
+        khat += G * group_bytes                   # the k̂ of every complete group
         scores += G * 4                           # one fp32 score written per group
         pt_score += (G + 15) // 16 * 4            # page ids read by the indexer
         pt += (L + Q - 1 + 63) // 64 * 4          # page ids of the request
         sel = 4 * min(g["topk_groups"], G) + (L + Q - 1 - 4 * G)
         kv += sel * kv_row                        # K and V rows of the selected tokens
     B = wl.batch
-    idx_q = B * (8 * 64 * 4 + 8 * 4)              # q_idx + w_idx
+    idx_q = B * (g["idx_heads"] * g["idx_dim"] * 4 + g["idx_heads"] * 4)  # q_idx + w_idx
     attn_io = B * Q * g["num_q_heads"] * g["head_dim"] * (2 + 4)  # bf16 q in, fp32 out
     return dict(khat=khat, kv=kv, scores=scores, page_table=pt,
                 step=khat + kv + pt + idx_q + attn_io,
@@ -230,6 +234,76 @@ def prefill_scoring(dev, steps: int, warmup: int) -> dict:
             "prefill_step_ms": ms_step}
 
 
+def mqa_indexer(dev, steps: int, warmup: int) -> dict:
+    """The multi-query indexer form (4 heads x 128 sharing one key head):
+    the decode step at the Flash-Next attention shape (B8 at 262,144 tokens,
+    Hq 24 / Hkv 2, FP8 KV, K = 2,048 groups) with its GEMV against the HBM
+    peak, and the long-prefill chunk's matrix-core scoring against the BF16
+    peak."""
+    import numpy as np
+    import torch
+    import learned_sparse_attention_amd as qsa
+    import workload
+    from tests import qsa_gpu as H
+
+    def timed(fn, n):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    wl = workload.decode_workload(0x51A6, [262144] * 8, num_q_heads=24, num_kv_heads=2,
+                                  kv_dtype="fp8", topk_groups=2048, indexer="mqa")
+    d = H.to_dev(wl, dev)
+    g = wl.geom
+    out = torch.empty((8, 1, 24, 256), dtype=torch.float32, device=dev)
+    ws = torch.empty(qsa.decode_workspace_size(g, 8, 1, wl.max_ctx), dtype=torch.uint8,
+                     device=dev)
+    sc = torch.empty((8, wl.max_ctx // 4), dtype=torch.float32, device=dev)
+    ms_step = timed(lambda: qsa.qsa_decode(g, d["k"], d["v"], d["khat"], d["pt"], d["ctx"],
+                                           d["q_idx"], d["w_idx"], d["q"], wl.max_ctx, out=out,
+                                           workspace=ws, num_pages=wl.num_pages), steps)
+    ms_gemv = timed(lambda: qsa.qsa_index_score(g, d["khat"], d["pt"], None, d["ctx"],
+                                                d["q_idx"], d["w_idx"], wl.max_ctx,
+                                                out_scores=sc, num_pages=wl.num_pages), steps)
+    ab = algorithmic_bytes(wl)
+    del d, out, ws, sc
+    pw = workload.prefill_workload(0x51A7, 28672, 4096, kv_dtype="bf16", topk_groups=512,
+                                   indexer="mqa")
+    pd = H.to_dev(pw, dev)
+    gstride = (pw.first_pos + pw.n_q) // 4
+    psc = torch.empty((pw.n_q, gstride), dtype=torch.float32, device=dev)
+    ms_pf = timed(lambda: qsa.qsa_index_score_prefill(pw.geom, pd["khat"], pd["pt"], pw.req,
+                                                      pw.first_pos, pd["q_idx"], pd["w_idx"],
+                                                      out_scores=psc, num_pages=pw.num_pages),
+                  max(5, steps // 2))
+    visible = int((pw.row_len.astype(np.int64) // 4).sum()) * 2 * 4 * 128
+    gemv_gbs = ab["score_kernel"] / (ms_gemv * 1e-3) / 1e9
+    step_gbs = ab["step"] / (ms_step * 1e-3) / 1e9
+    tflops = visible / (ms_pf * 1e-3) / 1e12
+    return {"indexer": "4 query heads x 128 dims sharing one key head (512 B of k-hat/group)",
+            "decode": {"workload": "decode B8, L=262,144, Hq 24 / Hkv 2, FP8 E4M3 KV, "
+                                   "K=2,048 groups",
+                       "layer_steps_per_s": 1e3 / ms_step, "ms_per_step": ms_step,
+                       "step_bytes": ab["step"], "step_frac": step_gbs / HBM_PEAK_GBS,
+                       "gemv_kernel": "index_score_gemv_mqa_kernel",
+                       "gemv_ms": ms_gemv, "gemv_bytes": ab["score_kernel"],
+                       "gemv_achieved": gemv_gbs, "gemv_frac": gemv_gbs / HBM_PEAK_GBS,
+                       "unit": "GB/s", "peak": HBM_PEAK_GBS},
+            "prefill_scoring": {"workload": "prefill chunk of 4,096 queries at positions "
+                                            "28,672..32,767, 8,192 groups",
+                                "kernel": "index_score_mfma_kernel<SharedKeyForm>",
+                                "achieved": tflops, "peak": BF16_PEAK_TFLOPS,
+                                "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS,
+                                "flops_per_launch": visible, "ms_per_launch": ms_pf}}
+
+
 def kv_append(dev, steps: int, warmup: int) -> dict:
     """The cache append of the long-prefill chunk: 4,096 new tokens' K and V
     (bf16, 2 KV heads x 256) written into an FP8 E4M3 paged cache at
@@ -272,7 +346,7 @@ def kv_append(dev, steps: int, warmup: int) -> dict:
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": "append of 4,096 tokens (positions 28,672..32,767) into an FP8 E4M3 "
                         "paged cache, 2 KV heads x 256, plus 1,024 k-hat groups",
-            "kernels": ["append_kv_kernel", "append_khat_kernel"], "bound": "hbm",
+            "kernel": "append_kernel", "bound": "hbm",
             "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
             "bytes_per_call": nbytes, "ms_per_call": ms}
 
@@ -412,6 +486,7 @@ def main() -> int:
     if not args.no_prefill:
         result["prefill_scoring"] = prefill_scoring(dev, max(5, args.steps // 2), 3)
         result["kv_append"] = kv_append(dev, max(20, args.steps), 5)
+        result["mqa_indexer"] = mqa_indexer(dev, max(10, args.steps // 2), 3)
     if args.calibrate_copy:
         calibrate_copy(dev)
     if not args.no_cpu_baseline:

@@ -93,8 +93,16 @@ __device__ __forceinline__ void store8(void* cache, long long dst, qsa_u4v x, fl
   }
 }
 
+__device__ __forceinline__ void append_khat(const AppendArgs& a, long long idx);
+
+// One launch does both parts: the first kv_blocks workgroups move K/V, the
+// rest the k̂ of completed groups.
 template <bool kFp8>
-__global__ __launch_bounds__(256) void append_kv_kernel(AppendArgs a) {
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a, int kv_blocks) {
+  if ((int)blockIdx.x >= kv_blocks) {
+    append_khat(a, (long long)(blockIdx.x - kv_blocks) * blockDim.x + threadIdx.x);
+    return;
+  }
   const int chunks = a.row_elems / 8;  // 16-byte pieces of a token's row
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long long)a.n_req * a.n_tokens * chunks) return;
@@ -113,10 +121,9 @@ __global__ __launch_bounds__(256) void append_kv_kernel(AppendArgs a) {
   store8<kFp8>(a.v_cache, dst, vx, a.v_scale);
 }
 
-__global__ __launch_bounds__(256) void append_khat_kernel(AppendArgs a) {
+__device__ __forceinline__ void append_khat(const AppendArgs& a, long long idx) {
   const int kF4 = a.group_f4;
-  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long long)a.n_req * a.khat_slots * kF4) return;
+  if (!a.khat_new || idx >= (long long)a.n_req * a.khat_slots * kF4) return;
   const long long slot = idx / kF4;  // request r, slot j
   const int f = (int)(idx - slot * kF4);
   const int r = (int)(slot / a.khat_slots), j = (int)(slot - (long long)r * a.khat_slots);
@@ -146,15 +153,10 @@ hipError_t launch_append(void* k_cache, void* v_cache, float* khat_cache,
                khat_group_floats / 4, row_elems, k_scale, v_scale};
   const long long n_kv = (long long)n_req * n_tokens * (row_elems / 8);
   const int blocks_kv = (int)((n_kv + 255) / 256);
-  if (kv_dtype == 1)
-    hipLaunchKernelGGL(append_kv_kernel<true>, dim3(blocks_kv), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(append_kv_kernel<false>, dim3(blocks_kv), dim3(256), 0, stream, a);
-  if (khat_new) {
-    const long long n_kh = (long long)n_req * a.khat_slots * a.group_f4;
-    hipLaunchKernelGGL(append_khat_kernel, dim3((int)((n_kh + 255) / 256)), dim3(256), 0, stream,
-                       a);
-  }
+  const long long n_kh = khat_new ? (long long)n_req * a.khat_slots * a.group_f4 : 0;
+  const int blocks = blocks_kv + (int)((n_kh + 255) / 256);
+  auto kern = kv_dtype == 1 ? append_kernel<true> : append_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, stream, a, blocks_kv);
   return hipGetLastError();
 }
 
