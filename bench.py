@@ -157,7 +157,8 @@ def write_counters(fetch_dir: str, write_dir: str, workload_name: str, commands:
         if f_ is None or w_ is None:
             continue
         tot = f_ * 1024.0 * ff + w_ * 1024.0 * fw
-        lines.append(f"| {k[:90]} | {f_:.0f} | {w_:.0f} | {tot:.0f} |")
+        short = k.replace("qsa::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        lines.append(f"| {short[:90]} | {f_:.0f} | {w_:.0f} | {tot:.0f} |")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", f"hbm_traffic__{workload_name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
