@@ -234,7 +234,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
   // ---- main loop: rounds of kNS sub-tiles per wave (sub-tiles
   // wave + 4*i); a round issues all of its loads before computing any of
   // them, so one memory latency covers kNS sub-tiles
-  constexpr int kNS = 2;
+  constexpr int kNS = kFp8 ? 2 : 1;
   for (int s0 = wave; s0 < n_sub; s0 += kNS * kAttnWaves) {
     SubTile<kFp8> bt[kNS];
 #pragma unroll
@@ -311,10 +311,15 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
   }
 }
 
+// Dynamic LDS: the row statistics, then one region that holds the query
+// tile and the token rows during the main loop and the per-wave
+// accumulators during the merge (the barrier before the merge writes
+// separates the two uses).
 constexpr int kQLdsElems = 16 * (kHeadDim + 8);
+constexpr int kMlFloats = (kAttnWaves + 1) * 32;
 
 template <bool kFp8>
-__global__ __launch_bounds__(kAttnThreads, kFp8 ? 2 : 1) void attn_decode_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_decode_kernel(AttnArgs a) {
   extern __shared__ float smem[];
   const int gq = a.Hq / a.Hkv;
   const int Q = a.q_per_req;
@@ -322,9 +327,9 @@ __global__ __launch_bounds__(kAttnThreads, kFp8 ? 2 : 1) void attn_decode_kernel
   const int nblk = (n_rows + 15) / 16;
   const int split = blockIdx.x / nblk, rb = blockIdx.x % nblk;
   const int kvh = blockIdx.y, b = blockIdx.z;
-  float* acc_lds = smem;
-  float* ml_lds = acc_lds + kAttnWaves * 16 * kAccPitch;
-  uint16_t* q_lds = reinterpret_cast<uint16_t*>(ml_lds + (kAttnWaves + 1) * 32);
+  float* ml_lds = smem;
+  float* acc_lds = smem + kMlFloats;
+  uint16_t* q_lds = reinterpret_cast<uint16_t*>(acc_lds);
   int32_t* tok_row = reinterpret_cast<int32_t*>(q_lds + kQLdsElems);
 
   const int L0 = a.ctx_lens[b];
@@ -348,13 +353,13 @@ __global__ __launch_bounds__(kAttnThreads, kFp8 ? 2 : 1) void attn_decode_kernel
 }
 
 template <bool kFp8>
-__global__ __launch_bounds__(kAttnThreads, kFp8 ? 2 : 1) void attn_prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs a) {
   extern __shared__ float smem[];
   const int qi = blockIdx.x, kvh = blockIdx.y;
   const int gq = a.Hq / a.Hkv;
-  float* acc_lds = smem;
-  float* ml_lds = acc_lds + kAttnWaves * 16 * kAccPitch;
-  uint16_t* q_lds = reinterpret_cast<uint16_t*>(ml_lds + (kAttnWaves + 1) * 32);
+  float* ml_lds = smem;
+  float* acc_lds = smem + kMlFloats;
+  uint16_t* q_lds = reinterpret_cast<uint16_t*>(acc_lds);
   int32_t* tok_row = reinterpret_cast<int32_t*>(q_lds + kQLdsElems);
 
   const int L = a.first_pos + qi + 1;
@@ -437,8 +442,10 @@ __global__ void expand_tokens_kernel(const int32_t* __restrict__ sel, int K,
 }
 
 size_t attn_smem_bytes(int stream_cap) {
-  return sizeof(float) * ((size_t)kAttnWaves * 16 * kAccPitch + (size_t)(kAttnWaves + 1) * 32) +
-         sizeof(uint16_t) * (size_t)kQLdsElems + sizeof(int32_t) * (size_t)((stream_cap + 15) / 16 * 16);
+  const size_t acc = sizeof(float) * (size_t)kAttnWaves * 16 * kAccPitch;
+  const size_t loop = sizeof(uint16_t) * (size_t)kQLdsElems +
+                      sizeof(int32_t) * (size_t)((stream_cap + 15) / 16 * 16);
+  return sizeof(float) * (size_t)kMlFloats + (acc > loop ? acc : loop);
 }
 
 template <bool kFp8>
