@@ -26,9 +26,11 @@
 //            If a slice overflowed or fewer than K candidates survived (the
 //            guess missed), the row is re-ranked exactly from the full score
 //            row instead, so the result never depends on the sample.
-// Shorter rows (up to 16,384 groups, e.g. prefill queries: thousands of
-// rows) skip the extract step: every group is a candidate of the finish
-// step.
+// Short rows (up to 8,192 groups: prefill queries, thousands of rows) take
+// one 256-thread workgroup each (row kernel): the row is pruned with the
+// same sampled guess inside the workgroup and only the candidates are
+// ranked.  Rows of 8,193 to 16,384 groups (a few decode rows) go straight
+// to the finish step with every group a candidate.
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
@@ -42,6 +44,9 @@ constexpr int kDirect = 16384;     // rows up to this length skip extraction
 constexpr int kMaxGroups = 65536;  // 262,144 tokens / 4
 constexpr int kMaxSlices = kMaxGroups / kSlice;
 constexpr int kFinishThreads = 1024;
+constexpr int kShort = 8192;       // rows up to this length: kShortThreads per row
+constexpr int kShortThreads = 256;
+constexpr int kRowCap = 4096;      // candidate slots of a short row
 constexpr int kExtractThreads = 256;
 constexpr int kBins = 4096;        // fallback value-linear bins
 
@@ -197,6 +202,102 @@ __device__ uint32_t candidate_threshold(const uint32_t (&key)[M], uint32_t need,
   return kmin + prefix;
 }
 
+// Exact threshold among the M keys per thread of a whole short row (0 =
+// empty slot): the need-th largest key T and how many copies of T are
+// taken.  Scores of a row crowd into a few binary exponents, so radix
+// digits of the keys would pile into a handful of histogram bins; the first
+// pass instead sorts the keys into 256 bins linear in the score between the
+// row's finite minimum and maximum (a monotone map of the key: -inf and
+// below to bin 0, +inf and above to bin 255), then radix passes over the
+// key offsets rank the keys of the bin that holds the need-th one.
+template <int NT, int M>
+__device__ uint32_t row_threshold(const uint32_t (&key)[M], uint32_t need, uint32_t* hist,
+                                  float* red, int* sh, uint32_t* take_eq) {
+  static_assert(M <= 32, "one bit per key in a mask");
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const uint32_t kneg = score_key(-INFINITY), kpos = score_key(INFINITY);
+  float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    if (key[m] > kneg && key[m] < kpos) {
+      const float v = key_value(key[m]);
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, o, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  }
+  if (lane == 0) { red[wid] = mn; red[NW + wid] = mx; }
+  for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+  if (tid == 0) { sh[2] = (int)0xFFFFFFFFu; sh[3] = 0; }
+  __syncthreads();
+  mn = red[0]; mx = red[NW];
+  for (int w = 1; w < NW; ++w) { mn = fminf(mn, red[w]); mx = fmaxf(mx, red[NW + w]); }
+  float scale = 0.0f;
+  if (mx > mn) {
+    scale = 256.0f / (mx - mn);
+    if (!(scale < INFINITY)) scale = 0.0f;
+  }
+  auto bin_of = [&](uint32_t k) -> uint32_t {
+    if (k <= kneg) return 0u;
+    if (k >= kpos) return 255u;
+    const float t = (key_value(k) - mn) * scale;
+    return (uint32_t)fminf(fmaxf(t, 0.0f), 255.0f);
+  };
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+    if (key[m]) atomicAdd(&hist[bin_of(key[m])], 1u);
+  __syncthreads();
+  uint32_t tb;
+  block_find256(hist, need, sh, &tb, &need);
+  // key range of the chosen bin, and which of this thread's keys lie in it
+  uint32_t in_bin = 0u, lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    if (key[m] && bin_of(key[m]) == tb) {
+      in_bin |= 1u << m;
+      lo = min(lo, key[m]);
+      hi = max(hi, key[m]);
+    }
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (lane == 0 && lo <= hi) {
+    atomicMin(reinterpret_cast<uint32_t*>(&sh[2]), lo);
+    atomicMax(reinterpret_cast<uint32_t*>(&sh[3]), hi);
+  }
+  __syncthreads();
+  lo = (uint32_t)sh[2];
+  hi = (uint32_t)sh[3];
+  const uint32_t span = hi - lo;
+  int nbits = span ? 32 - __clz(span) : 0;
+  uint32_t prefix = 0, pmask = 0;  // over offsets key - lo
+  while (nbits > 0) {
+    const int sft = nbits > 8 ? nbits - 8 : 0;
+    const uint32_t dmask = (1u << (nbits - sft)) - 1u;
+    for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const uint32_t off = key[m] - lo;
+      if (((in_bin >> m) & 1u) && (off & pmask) == prefix)
+        atomicAdd(&hist[(off >> sft) & dmask], 1u);
+    }
+    __syncthreads();
+    uint32_t d;
+    block_find256(hist, need, sh, &d, &need);
+    prefix |= d << sft;
+    pmask |= dmask << sft;
+    nbits = sft;
+  }
+  *take_eq = need;
+  return lo + prefix;
+}
+
 // Exact threshold over all G scores of a row, streamed from memory in
 // every pass (the rare path taken when the pruning guess misses): the
 // need-th largest key T and how many copies of T are taken.  Keys are
@@ -305,6 +406,49 @@ __device__ uint32_t exact_threshold_stream(const float* srow, int G, uint32_t ne
   }
   *take_eq = need;
   return lo + prefix;
+}
+
+// The groups marked in selmap, plus the first take_eq (in index order) of
+// those marked in eqmap, written in ascending order to orow[0, K).  Thread
+// t owns bitmap words [WPT t, WPT t + WPT); two block scans place them.
+template <int NT, int WPT>
+__device__ __forceinline__ void emit_selection(const uint32_t* selmap, const uint32_t* eqmap,
+                                               int nwords, uint32_t take_eq, int K,
+                                               int32_t* orow, uint32_t* tmp) {
+  const int tid = threadIdx.x;
+  uint32_t sw[WPT], ew[WPT];
+  uint32_t n_eq = 0;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int w = tid * WPT + i;
+    sw[i] = w < nwords ? selmap[w] : 0u;
+    ew[i] = w < nwords ? eqmap[w] : 0u;
+    n_eq += (uint32_t)__popc(ew[i]);
+  }
+  uint32_t eq_before = block_excl_scan<NT>(n_eq, tmp);
+  uint32_t n_sel = 0;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    uint32_t w = ew[i];
+    while (w) {
+      const uint32_t bit = w & (~w + 1u);
+      if (eq_before < take_eq) sw[i] |= bit;
+      ++eq_before;
+      w ^= bit;
+    }
+    n_sel += (uint32_t)__popc(sw[i]);
+  }
+  uint32_t pos = block_excl_scan<NT>(n_sel, tmp);
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    uint32_t w = sw[i];
+    while (w) {
+      const int b = __ffs(w) - 1;
+      if (pos < (uint32_t)K) orow[pos] = 32 * (tid * WPT + i) + b;
+      ++pos;
+      w &= w - 1u;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -419,15 +563,16 @@ __global__ __launch_bounds__(kExtractThreads) void topk_extract_kernel(
 // ---------------------------------------------------------------------------
 // finish: one workgroup per row
 
-template <bool kFromCand, int MC>
-__global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
+template <bool kFromCand, int MC, int NT, int kMaxG>
+__global__ __launch_bounds__(NT) void topk_finish_kernel(
     const float* __restrict__ scores, int gstride, const int32_t* __restrict__ row_len,
     int first_pos, int max_ctx, int K, const uint32_t* __restrict__ cand_val,
     const uint16_t* __restrict__ cand_idx, const int32_t* __restrict__ cand_cnt,
     int32_t* __restrict__ out) {
-  constexpr int NT = kFinishThreads, NW = NT / kWave;
-  constexpr int kW = kMaxGroups / 32;
-  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
+  constexpr int NW = NT / kWave;
+  constexpr int kW = kMaxG / 32 > NT ? kMaxG / 32 : NT;  // bitmap words (at least one per thread)
+  // the value-linear bins serve only the re-ranking of candidate rows
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kFromCand ? kBins : 256];
   __shared__ uint32_t selmap[kW];
   __shared__ uint32_t eqmap[kW];
   __shared__ uint32_t tmp[2 * NW + 1];
@@ -489,14 +634,17 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
       cg[m] = (uint32_t)i;
     }
   }
-  uint32_t T, take_eq;
-  if (ok) {
-    T = candidate_threshold<NT, MC>(ck, (uint32_t)K, hist, tmp, sh, &take_eq);
+  uint32_t T = 0, take_eq = 0;
+  if (!kFromCand || ok) {
+    if constexpr (kFromCand)
+      T = candidate_threshold<NT, MC>(ck, (uint32_t)K, hist, tmp, sh, &take_eq);
+    else
+      T = row_threshold<NT, MC>(ck, (uint32_t)K, hist, red, sh, &take_eq);
 #pragma unroll
     for (int m = 0; m < MC; ++m)
       if (ck[m] >= T && ck[m]) atomicOr(ck[m] > T ? &selmap[cg[m] >> 5] : &eqmap[cg[m] >> 5],
                                         1u << (cg[m] & 31));
-  } else {
+  } else if constexpr (kFromCand) {
     // the pruning guess missed: exact ranking of the whole row
     T = exact_threshold_stream<NT>(srow, G, (uint32_t)K, hist, red, sh, &take_eq);
     for (int i = tid; i < G; i += NT) {
@@ -506,41 +654,188 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
   }
   __syncthreads();
 
-  // bitmaps -> ascending indices; thread t owns words [2t, 2t + 2)
-  constexpr int WPT = kW / NT;
-  uint32_t sw[WPT], ew[WPT];
-  uint32_t n_eq = 0;
+  emit_selection<NT, kW / NT>(selmap, eqmap, nwords, take_eq, K, orow, tmp);
+}
+
+// ---------------------------------------------------------------------------
+// row: one workgroup per short row (thousands of them in a prefill chunk).
+// Ranking every key of the row costs several ALU operations per key and
+// pass, so the row is pruned first, as the extract step prunes a slice:
+// the guess is the exact r-th largest of 512 evenly spaced sample keys,
+// every key >= guess is compacted into LDS (about K + 4 sqrt(K) of the
+// row), and only those are ranked.  If a wave's candidates overflow its
+// LDS region or fewer than K survive, the whole row is ranked instead.
+
+// The need-th largest of the candidate keys (all >= kmin, at most kmax;
+// 0 = empty slot; only the first `active` slots of each thread can be
+// occupied) and how many copies of it are taken: radix passes of 8 bits
+// over the offsets key - kmin.
+template <int NT, int M>
+__device__ uint32_t pruned_threshold(const uint32_t (&key)[M], int active, uint32_t kmin,
+                                     uint32_t kmax, uint32_t need, uint32_t* hist, int* sh,
+                                     uint32_t* take_eq) {
+  const int tid = threadIdx.x;
+  const uint32_t span = kmax - kmin;
+  int nbits = span ? 32 - __clz(span) : 0;
+  uint32_t prefix = 0, pmask = 0;
+  while (nbits > 0) {
+    const int sft = nbits > 8 ? nbits - 8 : 0;
+    const uint32_t dmask = (1u << (nbits - sft)) - 1u;
+    for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+    __syncthreads();
 #pragma unroll
-  for (int i = 0; i < WPT; ++i) {
-    const int w = tid * WPT + i;
-    sw[i] = w < nwords ? selmap[w] : 0u;
-    ew[i] = w < nwords ? eqmap[w] : 0u;
-    n_eq += (uint32_t)__popc(ew[i]);
-  }
-  uint32_t eq_before = block_excl_scan<NT>(n_eq, tmp);
-  uint32_t n_sel = 0;
-#pragma unroll
-  for (int i = 0; i < WPT; ++i) {
-    uint32_t w = ew[i];
-    while (w) {
-      const uint32_t bit = w & (~w + 1u);
-      if (eq_before < take_eq) sw[i] |= bit;
-      ++eq_before;
-      w ^= bit;
+    for (int m = 0; m < M; ++m) {
+      if (m < active) {
+        const uint32_t off = key[m] - kmin;
+        if (key[m] && (off & pmask) == prefix) atomicAdd(&hist[(off >> sft) & dmask], 1u);
+      }
     }
-    n_sel += (uint32_t)__popc(sw[i]);
+    __syncthreads();
+    uint32_t d;
+    block_find256(hist, need, sh, &d, &need);
+    prefix |= d << sft;
+    pmask |= dmask << sft;
+    nbits = sft;
   }
-  uint32_t pos = block_excl_scan<NT>(n_sel, tmp);
+  *take_eq = need;
+  return kmin + prefix;
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_row_kernel(const float* __restrict__ scores,
+                                                      int gstride,
+                                                      const int32_t* __restrict__ row_len,
+                                                      int first_pos, int max_ctx, int K,
+                                                      int32_t* __restrict__ out) {
+  constexpr int NW = NT / kWave;
+  constexpr int E = kShort / (4 * NT);  // 16-byte chunks per thread
+  constexpr int M = 4 * E;              // keys per thread: key 4e + c is group 4 (e NT + t) + c
+  constexpr int kW = kShort / 32 > NT ? kShort / 32 : NT;  // bitmap words
+  constexpr int kCW = kRowCap / NW;     // candidate slots per wave
+  constexpr int MC = kRowCap / NT;      // candidate slots per thread
+  __shared__ __attribute__((aligned(16))) uint32_t hist[256];
+  __shared__ uint32_t selmap[kW];
+  __shared__ uint32_t eqmap[kW];
+  __shared__ uint32_t cval[kRowCap];
+  __shared__ uint16_t cidx[kRowCap];
+  __shared__ uint32_t wcnt[NW];
+  __shared__ uint32_t tmp[2 * NW + 1];
+  __shared__ float red[2 * NW];
+  __shared__ int sh[4];
+
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int L = row_len ? row_len[row] : first_pos + row + 1;
+  int G = (L >= 0 && L <= max_ctx) ? L / kRatio : 0;
+  if (G > gstride) G = gstride;
+  int32_t* orow = out + (size_t)row * K;
+  if (G <= K) {  // every complete group is kept
+    for (int i = tid; i < K; i += NT) orow[i] = (i < G) ? i : -1;
+    return;
+  }
+  // the row's scores (addresses clamped into the row instead of branching
+  // per lane; entries past its groups are masked below) and, for wave 0,
+  // the sample, all issued together
+  const float* srow = scores + (size_t)row * gstride;
+  uint32_t ck[M];
+  if ((gstride & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15u) == 0u) {
 #pragma unroll
-  for (int i = 0; i < WPT; ++i) {
-    uint32_t w = sw[i];
-    while (w) {
-      const int b = __ffs(w) - 1;
-      if (pos < (uint32_t)K) orow[pos] = 32 * (tid * WPT + i) + b;
-      ++pos;
-      w &= w - 1u;
+    for (int e = 0; e < E; ++e) {
+      const float4 f = *reinterpret_cast<const float4*>(srow + min(4 * (e * NT + tid), gstride - 4));
+      ck[4 * e] = __float_as_uint(f.x); ck[4 * e + 1] = __float_as_uint(f.y);
+      ck[4 * e + 2] = __float_as_uint(f.z); ck[4 * e + 3] = __float_as_uint(f.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < M; ++j)
+      ck[j] = __float_as_uint(srow[min(4 * ((j >> 2) * NT + tid) + (j & 3), gstride - 1)]);
+  }
+  float sv[8];
+  if (wid == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sv[i] = srow[(int)(((long long)(lane + kWave * i) * G) / kSample)];
+  }
+  const int nwords = (G + 31) / 32;
+  for (int i = tid; i < nwords; i += NT) { selmap[i] = 0u; eqmap[i] = 0u; }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int lim = G - 4 * (e * NT + tid);  // keys of chunk e below G
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      ck[4 * e + c] = c < lim ? score_key(__uint_as_float(ck[4 * e + c])) : 0u;
+  }
+  if (wid == 0) {
+    uint32_t sk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sk[i] = score_key(sv[i]);
+    const int r0 = (int)(((long long)kSample * K + G - 1) / G);
+    int r = r0 + 4 * (int)ceilf(sqrtf((float)r0)) + 4;
+    if (r > kSample) r = kSample;
+    const uint32_t gk = wave_select_rth(sk, (uint32_t)r, hist);
+    if (lane == 0) { sh[0] = (int)gk; sh[3] = 0; }
+  }
+  __syncthreads();
+  const uint32_t gk = (uint32_t)sh[0];
+  // keys >= guess, each wave into its own region, in order; the largest
+  // candidate key bounds the radix passes
+  uint32_t run = 0, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    const bool pred = ck[j] >= gk && ck[j] != 0u;
+    const uint64_t bm = __ballot(pred);
+    const uint32_t pos = run + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+    if (pred && pos < (uint32_t)kCW) {
+      cval[wid * kCW + pos] = ck[j];
+      cidx[wid * kCW + pos] = (uint16_t)(4 * ((j >> 2) * NT + tid) + (j & 3));
+    }
+    if (pred) kmax = max(kmax, ck[j]);
+    run += (uint32_t)__popcll(bm);
+  }
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) {
+    wcnt[wid] = run;
+    atomicMax(reinterpret_cast<uint32_t*>(&sh[3]), kmax);
+  }
+  __syncthreads();
+  uint32_t total = 0, most = 0;
+  bool over = false;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    total += wcnt[w];
+    most = max(most, wcnt[w]);
+    over |= wcnt[w] > (uint32_t)kCW;
+  }
+  uint32_t T = 0, take_eq = 0;
+  if (!over && total >= (uint32_t)K) {
+    // candidate m of this thread is slot row m / NW of wave region m % NW;
+    // only the first `active` slot rows of a region can be occupied
+    const int active = (int)((most + NT - 1) / NT);
+    auto slot = [&](int m) { return (m % NW) * kCW + (m / NW) * NT + tid; };
+    uint32_t c[MC];
+#pragma unroll
+    for (int m = 0; m < MC; ++m)
+      c[m] = m / NW < active && (uint32_t)((m / NW) * NT + tid) < wcnt[m % NW] ? cval[slot(m)] : 0u;
+    T = pruned_threshold<NT, MC>(c, active * NW, gk, (uint32_t)sh[3], (uint32_t)K, hist, sh,
+                                 &take_eq);
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      if (c[m] >= T && c[m]) {
+        const uint32_t g = cidx[slot(m)];
+        atomicOr(c[m] > T ? &selmap[g >> 5] : &eqmap[g >> 5], 1u << (g & 31));
+      }
+    }
+  } else {
+    // the guess missed: rank the whole row
+    T = row_threshold<NT, M>(ck, (uint32_t)K, hist, red, sh, &take_eq);
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      const uint32_t g = (uint32_t)(4 * ((j >> 2) * NT + tid) + (j & 3));
+      if (ck[j] >= T && ck[j]) atomicOr(ck[j] > T ? &selmap[g >> 5] : &eqmap[g >> 5], 1u << (g & 31));
     }
   }
+  __syncthreads();
+  emit_selection<NT, kW / NT>(selmap, eqmap, nwords, take_eq, K, orow, tmp);
 }
 
 }  // namespace
@@ -557,10 +852,16 @@ hipError_t launch_topk(const float* scores, int gstride, int n_rows, const int32
                        hipStream_t stream, const float* samples) {
   if (n_rows <= 0) return hipSuccess;
   if (gstride > kMaxGroups) return hipErrorInvalidValue;
+  if (gstride <= kShort) {
+    // many short rows (prefill): small workgroups, several rows per CU
+    hipLaunchKernelGGL((topk_row_kernel<kShortThreads>), dim3(n_rows), dim3(kShortThreads), 0,
+                       stream, scores, gstride, row_len, first_pos, max_ctx, K, out);
+    return hipGetLastError();
+  }
   if (gstride <= kDirect) {
-    hipLaunchKernelGGL((topk_finish_kernel<false, kDirect / kFinishThreads>), dim3(n_rows),
-                       dim3(kFinishThreads), 0, stream, scores, gstride, row_len, first_pos,
-                       max_ctx, K, nullptr, nullptr, nullptr, out);
+    hipLaunchKernelGGL((topk_finish_kernel<false, kDirect / kFinishThreads, kFinishThreads, kDirect>),
+                       dim3(n_rows), dim3(kFinishThreads), 0, stream, scores, gstride, row_len,
+                       first_pos, max_ctx, K, nullptr, nullptr, nullptr, out);
     return hipGetLastError();
   }
   if (!ws) return hipErrorInvalidValue;
@@ -577,7 +878,8 @@ hipError_t launch_topk(const float* scores, int gstride, int n_rows, const int32
                      samples);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((topk_finish_kernel<true, kMaxSlices * kSliceCap / kFinishThreads>),
+  hipLaunchKernelGGL((topk_finish_kernel<true, kMaxSlices * kSliceCap / kFinishThreads,
+                                          kFinishThreads, kMaxGroups>),
                      dim3(n_rows), dim3(kFinishThreads), 0, stream, scores, gstride, row_len,
                      first_pos, max_ctx, K, cval, cidx, ccnt, out);
   return hipGetLastError();

@@ -201,3 +201,48 @@ def test_decode_long_rows_coarse_scores(gpu):
     wl.q_idx[:] = np.round(wl.q_idx)
     wl.w_idx[:] = 0.5
     _decode_check(wl, gpu)
+
+
+# Rows of up to 8,192 groups (prefill queries, shorter decode) take the
+# one-workgroup pruned top-K: a sampled guess, candidates compacted into
+# LDS, and the whole row ranked instead when the guess misses.
+
+def test_decode_short_rows_sample_miss(gpu):
+    # the 512 sample positions of an 8,192-group row are its top scorers,
+    # so at K = 1,024 the guess keeps about 100 candidates and the whole-row
+    # ranking must take over
+    wl = workload.decode_workload(620, [32768, 32768 - 5], kv_dtype="fp8", topk_groups=1024)
+    gpp = 16
+    for b, L in enumerate(wl.ctx_lens):
+        G = int(L) // 4
+        for i in range(512):
+            g = (i * G) // 512
+            page = wl.page_table[b, g // gpp]
+            wl.khat[page, g % gpp] = 4.0 * wl.q_idx[b]
+    _decode_check(wl, gpu)
+
+
+def test_decode_short_rows_all_tied(gpu):
+    # all scores +0: every group is a candidate, the waves' LDS regions
+    # overflow, and the whole-row ranking must keep the lowest K indices
+    wl = workload.decode_workload(621, [32768, 20001], kv_dtype="bf16", topk_groups=2048)
+    wl.w_idx[:] = 0.0
+    _decode_check(wl, gpu)
+
+
+def test_decode_short_rows_coarse_scores(gpu):
+    # scores on a coarse grid: long runs of exact ties at the K-th score
+    wl = workload.decode_workload(622, [32768, 24000, 9001], kv_dtype="bf16", topk_groups=512)
+    wl.khat[:] = np.round(wl.khat)
+    wl.q_idx[:] = np.round(wl.q_idx)
+    wl.w_idx[:] = 0.5
+    _decode_check(wl, gpu)
+
+
+def test_decode_short_rows_odd_stride(gpu):
+    # a score row stride that is not a multiple of 4 (scalar loads in the
+    # short-row top-K), with rows at, just above and well above K groups
+    wl = workload.decode_workload(623, [4 * 5001 + 3, 4 * 512, 4 * 513 + 1, 4 * 3000],
+                                  kv_dtype="fp8", topk_groups=512)
+    assert wl.gstride % 4 != 0
+    _decode_check(wl, gpu)
