@@ -49,6 +49,7 @@ constexpr int kShortThreads = 256;
 constexpr int kRowCap = 4096;      // candidate slots of a short row
 constexpr int kExtractThreads = 256;
 constexpr int kBins = 4096;        // fallback value-linear bins
+constexpr int kInfo = 4;           // per (row, slice): count, largest key, guess key, unused
 
 // Inclusive prefix sum across the 64 lanes of a wavefront with DPP: four
 // row shifts build 16-lane prefix sums, then row broadcasts of lanes 15 and
@@ -408,6 +409,71 @@ __device__ uint32_t exact_threshold_stream(const float* srow, int G, uint32_t ne
   return lo + prefix;
 }
 
+// Wave-level search of a 4,096-bin histogram for the bin holding the
+// need-th largest element: count(bins > b) < need <= count(bins >= b).
+// Lane l first sums the 64 bins of chunk 63 - l (lane 0: the top chunk),
+// then each lane takes one bin of the chosen chunk.
+__device__ __forceinline__ void wave_find4096(const uint32_t* hist, uint32_t need, uint32_t* bin,
+                                              uint32_t* rem) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint4* h4 = reinterpret_cast<const uint4*>(hist) + 16 * (63 - lane);
+  uint32_t part = 0u;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const uint4 v = h4[q];
+    part += (v.x + v.y) + (v.z + v.w);
+  }
+  uint32_t incl = wave_incl_scan(part);
+  uint64_t m = __ballot(incl - part < need && need <= incl);
+  int src = m ? __ffsll((unsigned long long)m) - 1 : 0;
+  const uint32_t need2 = need - ((uint32_t)__shfl((int)incl, src, kWave) -
+                                 (uint32_t)__shfl((int)part, src, kWave));
+  const int chunk = 63 - src;
+  const uint32_t c = hist[64 * chunk + 63 - lane];
+  incl = wave_incl_scan(c);
+  m = __ballot(incl - c < need2 && need2 <= incl);
+  src = m ? __ffsll((unsigned long long)m) - 1 : 0;
+  *bin = (uint32_t)(64 * chunk + 63 - src);
+  *rem = need2 - ((uint32_t)__shfl((int)incl, src, kWave) - (uint32_t)__shfl((int)c, src, kWave));
+}
+
+// The need-th largest of M candidate keys per thread (0 = empty slot), all
+// within [kmin, kmax], and how many copies of it are taken: radix passes of
+// up to 12 bits over the offsets key - kmin (two passes for spans up to
+// 2^24), with a 4,096-bin LDS histogram.
+template <int NT, int M>
+__device__ uint32_t wide_threshold(const uint32_t (&key)[M], uint32_t kmin, uint32_t kmax,
+                                   uint32_t need, uint32_t* hist, int* sh, uint32_t* take_eq) {
+  const int tid = threadIdx.x;
+  const uint32_t span = kmax >= kmin ? kmax - kmin : 0u;
+  int nbits = span ? 32 - __clz(span) : 0;
+  uint32_t prefix = 0, pmask = 0;
+  while (nbits > 0) {
+    const int sft = nbits > 12 ? nbits - 12 : 0;
+    const uint32_t dmask = (1u << (nbits - sft)) - 1u;
+    for (int i = tid; i < 4096; i += NT) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const uint32_t off = key[m] - kmin;
+      if (key[m] && (off & pmask) == prefix) atomicAdd(&hist[(off >> sft) & dmask], 1u);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      uint32_t b, r;
+      wave_find4096(hist, need, &b, &r);
+      if (tid == 0) { sh[0] = (int)b; sh[1] = (int)r; }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sh[0] << sft;
+    need = (uint32_t)sh[1];
+    pmask |= dmask << sft;
+    nbits = sft;
+  }
+  *take_eq = need;
+  return kmin + prefix;
+}
+
 // The groups marked in selmap, plus the first take_eq (in index order) of
 // those marked in eqmap, written in ascending order to orow[0, K).  Thread
 // t owns bitmap words [WPT t, WPT t + WPT); two block scans place them.
@@ -467,6 +533,7 @@ __global__ __launch_bounds__(kExtractThreads) void topk_extract_kernel(
   __shared__ uint32_t sval[kSliceCap];
   __shared__ uint16_t sidx[kSliceCap];
   __shared__ uint32_t wcnt[NW];
+  __shared__ uint32_t wmax[NW];
   __shared__ float sguess;
 
   const int slice = blockIdx.x, row = blockIdx.y;
@@ -501,8 +568,9 @@ __global__ __launch_bounds__(kExtractThreads) void topk_extract_kernel(
   const int L = row_len ? row_len[row] : first_pos + row + 1;
   int G = (L >= 0 && L <= max_ctx) ? L / kRatio : 0;
   if (G > gstride) G = gstride;
+  int32_t* info = cand_cnt + (size_t)(row * kMaxSlices + slice) * kInfo;
   if (G <= K || g0 >= G) {  // finish handles the row alone / empty slice
-    if (tid == 0) cand_cnt[row * kMaxSlices + slice] = 0;
+    if (tid == 0) { info[0] = 0; info[1] = 0; info[2] = 0; }
     return;
   }
 #pragma unroll
@@ -523,13 +591,17 @@ __global__ __launch_bounds__(kExtractThreads) void topk_extract_kernel(
     int r = r0 + 4 * (int)ceilf(sqrtf((float)r0)) + 4;
     if (r > kSample) r = kSample;
     const uint32_t gk = wave_select_rth(sk, (uint32_t)r, hist);
-    if (lane == 0) sguess = key_value(gk);
+    if (lane == 0) {
+      sguess = key_value(gk);
+      info[2] = (int32_t)gk;
+    }
   }
   __syncthreads();
   const float guess = sguess;
 
   // keep scores >= guess, each wave in its own region, in order
   uint32_t run = 0;
+  float kmx_f = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 4 * E4; ++e) {
     const bool pred = __uint_as_float(v[e]) >= guess;
@@ -540,9 +612,11 @@ __global__ __launch_bounds__(kExtractThreads) void topk_extract_kernel(
       sval[wid * kCW + pos] = v[e];
       sidx[wid * kCW + pos] = (uint16_t)(g0 + 4 * ((e / 4) * NT + tid) + (e % 4));
     }
+    if (pred) kmx_f = fmaxf(kmx_f, __uint_as_float(v[e]));  // kept scores are not NaN
     run += (uint32_t)__popcll(mask);
   }
-  if (lane == 0) wcnt[wid] = run;
+  const uint32_t kmx = wave_max_u32(run ? score_key(kmx_f) : 0u);  // score_key is monotone
+  if (lane == 0) { wcnt[wid] = run; wmax[wid] = kmx; }
   __syncthreads();
   uint32_t before = 0, total = 0;
   bool over = false;
@@ -557,7 +631,12 @@ __global__ __launch_bounds__(kExtractThreads) void topk_extract_kernel(
       cand_idx[slot0 + before + i] = sidx[wid * kCW + i];
     }
   }
-  if (tid == 0) cand_cnt[row * kMaxSlices + slice] = over ? kSliceCap + 1 : (int)total;
+  if (tid == 0) {
+    uint32_t m = 0u;
+    for (int w = 0; w < NW; ++w) m = max(m, wmax[w]);
+    info[0] = over ? kSliceCap + 1 : (int)total;
+    info[1] = (int32_t)m;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -587,16 +666,20 @@ __global__ __launch_bounds__(NT) void topk_finish_kernel(
   uint32_t ck[MC];
   uint32_t cg[MC];
   int cnt[MC];
+  uint32_t kmx[MC];
+  uint32_t gk = 0u;  // the guess: every candidate key is >= gk
   if (kFromCand) {
     static_assert(!kFromCand || kSliceCap == NT, "one slice per slot row");
     static_assert(!kFromCand || MC == kMaxSlices, "one count per slot row");
     const size_t base = (size_t)row * kMaxSlices * kSliceCap;
 #pragma unroll
     for (int m = 0; m < MC; ++m) {
-      cnt[m] = cand_cnt[row * kMaxSlices + m];
+      cnt[m] = cand_cnt[(size_t)(row * kMaxSlices + m) * kInfo];
+      kmx[m] = (uint32_t)cand_cnt[(size_t)(row * kMaxSlices + m) * kInfo + 1];
       ck[m] = cand_val[base + m * NT + tid];
       cg[m] = cand_idx[base + m * NT + tid];
     }
+    gk = (uint32_t)cand_cnt[(size_t)row * kMaxSlices * kInfo + 2];
   }
   const int L = row_len ? row_len[row] : first_pos + row + 1;
   int G = (L >= 0 && L <= max_ctx) ? L / kRatio : 0;
@@ -636,8 +719,12 @@ __global__ __launch_bounds__(NT) void topk_finish_kernel(
   }
   uint32_t T = 0, take_eq = 0;
   if (!kFromCand || ok) {
-    if constexpr (kFromCand)
-      T = candidate_threshold<NT, MC>(ck, (uint32_t)K, hist, tmp, sh, &take_eq);
+    if constexpr (kFromCand) {
+      uint32_t kmax = 0u;
+#pragma unroll
+      for (int m = 0; m < MC; ++m) kmax = max(kmax, cnt[m] > 0 ? kmx[m] : 0u);
+      T = wide_threshold<NT, MC>(ck, gk, kmax, (uint32_t)K, hist, sh, &take_eq);
+    }
     else
       T = row_threshold<NT, MC>(ck, (uint32_t)K, hist, red, sh, &take_eq);
 #pragma unroll
@@ -844,7 +931,7 @@ size_t topk_workspace_bytes(int n_rows, int gstride) {
   if (gstride <= kDirect) return 0;
   const size_t slots = (size_t)n_rows * kMaxSlices * kSliceCap;
   return slots * sizeof(uint32_t) + slots * sizeof(uint16_t) +
-         (size_t)n_rows * kMaxSlices * sizeof(int32_t) + 3 * 256;
+         (size_t)n_rows * kMaxSlices * kInfo * sizeof(int32_t) + 3 * 256;
 }
 
 hipError_t launch_topk(const float* scores, int gstride, int n_rows, const int32_t* row_len,
