@@ -93,16 +93,39 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
   const int n_stream = 4 * n_groups + n_extra;
   const int n_sub = (n_stream + 15) / 16;
   const int32_t* pt = a.page_table + (size_t)it.req * a.max_pages;
-  for (int i = tid; i < n_sub * 16; i += kAttnThreads) {
-    int t = -1;
-    if (i < 4 * n_groups) {
-      const int g = it.sel[it.g_begin + i / 4];
-      t = g >= 0 ? 4 * g + (i & 3) : -1;
-    } else if (i < n_stream) {
-      t = it.x_begin + (i - 4 * n_groups);
+  // Selected groups: a group's 4 tokens share one page (4 divides the page
+  // size), so each thread takes whole groups, kGroupBatch at a time, with
+  // all their selection loads issued before any page-table load: a long
+  // (prefill) selection then costs two memory round trips per batch, not
+  // two per token.
+  constexpr int kGroupBatch = 4;
+  for (int j0 = 0; j0 < n_groups; j0 += kGroupBatch * kAttnThreads) {
+    int gs[kGroupBatch], ph[kGroupBatch];
+#pragma unroll
+    for (int u = 0; u < kGroupBatch; ++u) {
+      const int j = j0 + u * kAttnThreads + tid;
+      gs[u] = j < n_groups ? it.sel[it.g_begin + j] : -1;
     }
+#pragma unroll
+    for (int u = 0; u < kGroupBatch; ++u) ph[u] = gs[u] >= 0 ? pt[(kRatio * gs[u]) / kPage] : -1;
+#pragma unroll
+    for (int u = 0; u < kGroupBatch; ++u) {
+      const int j = j0 + u * kAttnThreads + tid;
+      if (j < n_groups) {
+        int4 r = make_int4(-1, -1, -1, -1);
+        if (gs[u] >= 0 && ph[u] >= 0 && ph[u] < a.num_pages) {
+          const int base = ph[u] * kPage + (kRatio * gs[u]) % kPage;
+          r = make_int4(base, base + 1, base + 2, base + 3);
+        }
+        *reinterpret_cast<int4*>(tok_row + kRatio * j) = r;
+      }
+    }
+  }
+  // the contiguous extra tokens, then padding to whole sub-tiles
+  for (int i = kRatio * n_groups + tid; i < n_sub * 16; i += kAttnThreads) {
     int r = -1;
-    if (t >= 0) {
+    if (i < n_stream) {
+      const int t = it.x_begin + (i - kRatio * n_groups);
       const int phys = pt[t / kPage];
       if (phys >= 0 && phys < a.num_pages) r = phys * kPage + (t % kPage);
     }
