@@ -14,7 +14,7 @@ the HBM peak, the multi-query indexer form (decode at the Flash-Next shape
 and prefill scoring), and the CPU oracle timed on this host as a reported
 baseline.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense BF16 MFMA (no sparsity)
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense FP32 MFMA (context for the prefill scoring)
 
 CONFIG_NAMES = {
     1: "decode B1, L=8,193, BF16 KV, identity pages, K=512 groups",
@@ -230,6 +231,7 @@ def prefill_scoring(dev, steps: int, warmup: int) -> dict:
                         "8,192 groups, 8 heads x 64, BF16 KV, K=512 groups",
             "kernel": "index_score_mfma_kernel", "bound": "mfma", "achieved": tflops,
             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS,
+            "frac_vs_fp32_mfma_peak": tflops / FP32_MFMA_PEAK_TFLOPS,
             "flops_per_launch": visible, "dense_tile_flops": dense, "ms_per_launch": ms,
             "score_bytes_written": wl.n_q * gstride * 4,
             "prefill_step_ms": ms_step}
@@ -376,8 +378,8 @@ def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
@@ -429,6 +431,19 @@ def main() -> int:
     e1.record()
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
+    # the spread of single steps, from an event pair around each step of a
+    # second loop (the timed region above carries no per-step events)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for a, b in ev:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    per_step_us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+
+    def pct(p):
+        return per_step_us[min(len(per_step_us) - 1, int(p * len(per_step_us)))]
 
     # dominant kernel alone: the indexer GEMV (one launch per call), timed
     # with events on the current stream, which is the stream it runs on
@@ -482,6 +497,7 @@ def main() -> int:
         "step_roofline": {"bound": "hbm", "algorithmic_bytes": ab["step"],
                           "achieved": step_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": step_gbs / HBM_PEAK_GBS},
+        "step_us": {"p10": pct(0.10), "p50": pct(0.50), "p90": pct(0.90)},
         "gen_seconds": round(t_gen, 1),
     }
     if not args.no_prefill:
