@@ -91,3 +91,31 @@ def test_append_argument_checks():
                              None) == -2
     assert [qsa.append_khat_slots(n) for n in (-1, 0, 1, 4, 5, 8, 4096)] == [0, 0, 1, 1, 2, 2,
                                                                            1024]
+
+
+def test_empty_inputs_succeed_without_touching_buffers():
+    # batch / chunk / row count 0: success, decided on the host before any
+    # pointer is read (the cache pointers are placeholders that are never
+    # dereferenced, and every tensor pointer is null)
+    lib = qsa.load()
+    g = qsa._geom(workload.geometry())
+    fake = ctypes.c_void_p(0x1000)
+    c = qsa.PagedCache(fake, fake, fake, fake, 4, 4)
+    assert lib.qsa_decode(ctypes.byref(g), ctypes.byref(c), 0, 1, 256, *([None] * 8), None, 0,
+                          None) == 0
+    assert lib.qsa_prefill(ctypes.byref(g), ctypes.byref(c), 0, 100, 0, *([None] * 7), None, 0,
+                           None) == 0
+    assert lib.qsa_index_topk(ctypes.byref(g), ctypes.byref(c), 0, 256, *([None] * 6), None, 0,
+                              None) == 0
+    assert lib.qsa_index_score(ctypes.byref(g), ctypes.byref(c), 0, 256, *([None] * 5),
+                               None) == 0
+    assert lib.qsa_index_score_prefill(ctypes.byref(g), ctypes.byref(c), 0, 100, 0, None, None,
+                                       None, None) == 0
+    # the same calls with work to do and null tensors are refused
+    assert lib.qsa_decode(ctypes.byref(g), ctypes.byref(c), 1, 1, 256, *([None] * 8), None, 0,
+                          None) == -1
+    assert lib.qsa_prefill(ctypes.byref(g), ctypes.byref(c), 0, 100, 1, *([None] * 7), None, 0,
+                           None) == -1
+    # a context beyond the page table's reach is refused even when empty
+    assert lib.qsa_decode(ctypes.byref(g), ctypes.byref(c), 0, 1, 4 * 64 + 1, *([None] * 8),
+                          None, 0, None) == -1
