@@ -395,8 +395,8 @@ def main() -> int:
         write_counters(*args.write_counters, WORKLOAD_SLUG[args.config], args.counter_commands)
         return 0
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (the QSA layer step is not sharded "
-              "here); run with --gpus 1", file=sys.stderr)
+        print("bench.py: the QSA layer step runs on one GPU (it is not sharded); "
+              "run with --gpus 1", file=sys.stderr)
         return 2
 
     import numpy as np
