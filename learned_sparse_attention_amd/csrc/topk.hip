@@ -26,6 +26,10 @@
 //            If a slice overflowed or fewer than K candidates survived (the
 //            guess missed), the row is re-ranked exactly from the full score
 //            row instead, so the result never depends on the sample.
+// Rows of up to 2,048 groups (short decode contexts, early prefill queries)
+// take one wavefront each: lane l holds 32 consecutive groups, the K-th key
+// comes from radix passes over a wave-owned histogram and the selection
+// from bit masks and wave scans.
 // Short rows (up to 8,192 groups: prefill queries, thousands of rows) take
 // one 256-thread workgroup each (row kernel): the row is pruned with the
 // same sampled guess inside the workgroup and only the candidates are
@@ -44,6 +48,7 @@ constexpr int kDirect = 16384;     // rows up to this length skip extraction
 constexpr int kMaxGroups = 65536;  // 262,144 tokens / 4
 constexpr int kMaxSlices = kMaxGroups / kSlice;
 constexpr int kFinishThreads = 1024;
+constexpr int kWaveRow = 2048;     // rows up to this length: one wavefront per row
 constexpr int kShort = 8192;       // rows up to this length: kShortThreads per row
 constexpr int kShortThreads = 256;
 constexpr int kRowCap = 4096;      // candidate slots of a short row
@@ -134,10 +139,12 @@ __device__ __forceinline__ void block_find256(const uint32_t* hist, uint32_t nee
   __syncthreads();
 }
 
-// r-th largest of 8 keys per lane of one wave (512 keys), exact: four
-// 8-bit radix passes with an LDS histogram owned by this wave alone (LDS
-// operations of one wave execute in order, so no barrier is needed).
-__device__ uint32_t wave_select_rth(const uint32_t (&k)[8], uint32_t r, uint32_t* hist) {
+// r-th largest of M keys per lane of one wave (64 M keys; key 0 = empty
+// slot never counts), exact: four 8-bit radix passes with an LDS histogram
+// owned by this wave alone (LDS operations of one wave execute in order, so
+// no barrier is needed).
+template <int M>
+__device__ uint32_t wave_select_rth(const uint32_t (&k)[M], uint32_t r, uint32_t* hist) {
   const int lane = threadIdx.x & (kWave - 1);
   uint32_t prefix = 0, pmask = 0;
 #pragma unroll
@@ -146,8 +153,8 @@ __device__ uint32_t wave_select_rth(const uint32_t (&k)[8], uint32_t r, uint32_t
     *reinterpret_cast<uint4*>(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if ((k[i] & pmask) == prefix) atomicAdd(&hist[(k[i] >> s) & 255u], 1u);
+    for (int i = 0; i < M; ++i)
+      if (k[i] && (k[i] & pmask) == prefix) atomicAdd(&hist[(k[i] >> s) & 255u], 1u);
     __builtin_amdgcn_wave_barrier();
     uint32_t b;
     wave_find256(hist, r, &b, &r);
@@ -156,6 +163,44 @@ __device__ uint32_t wave_select_rth(const uint32_t (&k)[8], uint32_t r, uint32_t
     pmask |= 255u << s;
   }
   return prefix;
+}
+
+// r-th largest of the M keys per lane of one wave (0 = empty slot), like
+// wave_select_rth, but with radix passes of 8 bits over the offsets
+// key - kmin within the span of the present keys: a row's scores share a
+// few binary exponents, so the top digit of the raw keys would send almost
+// every key to two or three bins and serialise the LDS atomics.
+template <int M>
+__device__ uint32_t wave_select_span(const uint32_t (&k)[M], uint32_t r, uint32_t* hist) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < M; ++i)
+    if (k[i]) { kmin = min(kmin, k[i]); kmax = max(kmax, k[i]); }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  const uint32_t span = kmax >= kmin ? kmax - kmin : 0u;
+  int nbits = span ? 32 - __clz(span) : 0;
+  uint32_t prefix = 0, pmask = 0;
+  while (nbits > 0) {
+    const int s = nbits > 8 ? nbits - 8 : 0;
+    const uint32_t dmask = (1u << (nbits - s)) - 1u;
+    *reinterpret_cast<uint4*>(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const uint32_t off = k[i] - kmin;
+      if (k[i] && (off & pmask) == prefix) atomicAdd(&hist[(off >> s) & dmask], 1u);
+    }
+    __builtin_amdgcn_wave_barrier();
+    uint32_t b;
+    wave_find256(hist, r, &b, &r);
+    __builtin_amdgcn_wave_barrier();
+    prefix |= b << s;
+    pmask |= dmask << s;
+    nbits = s;
+  }
+  return kmin + prefix;
 }
 
 // Exact threshold among M candidate keys per thread (0 = empty slot):
@@ -925,6 +970,71 @@ __global__ __launch_bounds__(NT) void topk_row_kernel(const float* __restrict__ 
   emit_selection<NT, kW / NT>(selmap, eqmap, nwords, take_eq, K, orow, tmp);
 }
 
+// ---------------------------------------------------------------------------
+// wave: one wavefront per row of up to 64 M groups (short decode contexts,
+// early prefill queries), four rows per workgroup.  Lane l owns groups
+// [M l, M l + M): the exact K-th key comes from four radix passes over a
+// histogram owned by the wave, and the selection is emitted from per-lane
+// bit masks with wave scans, so no barrier is involved.
+
+template <int M>
+__global__ __launch_bounds__(kWave * 4) void topk_wave_kernel(const float* __restrict__ scores,
+                                                             int gstride,
+                                                             const int32_t* __restrict__ row_len,
+                                                             int first_pos, int max_ctx, int n_rows,
+                                                             int K, int32_t* __restrict__ out) {
+  static_assert(M % 4 == 0 && M <= 64, "groups per lane");
+  __shared__ __attribute__((aligned(16))) uint32_t hist_all[4][256];
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int row = blockIdx.x * 4 + wid;
+  if (row >= n_rows) return;  // whole wavefronts leave; nothing below synchronises the block
+  uint32_t* hist = hist_all[wid];
+  const int L = row_len ? row_len[row] : first_pos + row + 1;
+  int G = (L >= 0 && L <= max_ctx) ? L / kRatio : 0;
+  if (G > gstride) G = gstride;
+  int32_t* orow = out + (size_t)row * K;
+  if (G <= K) {  // every complete group is kept
+    for (int i = lane; i < K; i += kWave) orow[i] = (i < G) ? i : -1;
+    return;
+  }
+  const float* srow = scores + (size_t)row * gstride;
+  const int g0 = M * lane;
+  uint32_t key[M];
+  if ((gstride & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15u) == 0u) {
+#pragma unroll
+    for (int e = 0; e < M / 4; ++e) {
+      // clamped into the row; entries past G are masked below
+      const float4 f = *reinterpret_cast<const float4*>(srow + min(g0 + 4 * e, gstride - 4));
+      key[4 * e] = __float_as_uint(f.x); key[4 * e + 1] = __float_as_uint(f.y);
+      key[4 * e + 2] = __float_as_uint(f.z); key[4 * e + 3] = __float_as_uint(f.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < M; ++j) key[j] = __float_as_uint(srow[min(g0 + j, gstride - 1)]);
+  }
+#pragma unroll
+  for (int j = 0; j < M; ++j) key[j] = g0 + j < G ? score_key(__uint_as_float(key[j])) : 0u;
+  const uint32_t T = wave_select_span<M>(key, (uint32_t)K, hist);
+  // groups above T are taken; of those equal to T, the lowest-indexed ones
+  // up to K in all
+  uint64_t gt = 0u, eq = 0u;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    gt |= (key[j] > T) ? 1ull << j : 0ull;
+    eq |= (key[j] == T && key[j] != 0u) ? 1ull << j : 0ull;
+  }
+  const uint32_t n_gt = (uint32_t)__popcll(gt), n_eq = (uint32_t)__popcll(eq);
+  const uint32_t gt_incl = wave_incl_scan(n_gt), eq_incl = wave_incl_scan(n_eq);
+  const uint32_t take_eq = (uint32_t)K - (uint32_t)__shfl((int)gt_incl, kWave - 1, kWave);
+  uint32_t eq_before = eq_incl - n_eq;
+  uint64_t sel = gt;
+  for (uint64_t w = eq; w && eq_before < take_eq; w &= w - 1u, ++eq_before) sel |= w & (~w + 1u);
+  const uint32_t n_sel = (uint32_t)__popcll(sel);
+  uint32_t pos = wave_incl_scan(n_sel) - n_sel;
+  for (uint64_t w = sel; w; w &= w - 1u, ++pos)
+    if (pos < (uint32_t)K) orow[pos] = g0 + __ffsll((unsigned long long)w) - 1;
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(int n_rows, int gstride) {
@@ -939,6 +1049,13 @@ hipError_t launch_topk(const float* scores, int gstride, int n_rows, const int32
                        hipStream_t stream, const float* samples) {
   if (n_rows <= 0) return hipSuccess;
   if (gstride > kMaxGroups) return hipErrorInvalidValue;
+  if (gstride <= kWaveRow) {
+    // short rows: one wavefront each, 32 groups per lane
+    hipLaunchKernelGGL((topk_wave_kernel<kWaveRow / kWave>), dim3((n_rows + 3) / 4),
+                       dim3(kWave * 4), 0, stream, scores, gstride, row_len, first_pos, max_ctx,
+                       n_rows, K, out);
+    return hipGetLastError();
+  }
   if (gstride <= kShort) {
     // many short rows (prefill): small workgroups, several rows per CU
     hipLaunchKernelGGL((topk_row_kernel<kShortThreads>), dim3(n_rows), dim3(kShortThreads), 0,

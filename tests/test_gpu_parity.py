@@ -246,3 +246,31 @@ def test_decode_short_rows_odd_stride(gpu):
                                   kv_dtype="fp8", topk_groups=512)
     assert wl.gstride % 4 != 0
     _decode_check(wl, gpu)
+
+
+# Rows of up to 2,048 groups take one wavefront each (exact radix select
+# over the row's key span, selection emitted from per-lane bit masks).
+
+def test_decode_wave_rows_coarse_scores(gpu):
+    # long runs of exact ties at the K-th score
+    wl = workload.decode_workload(630, [8192, 6001, 4099], kv_dtype="bf16", topk_groups=512)
+    wl.khat[:] = np.round(wl.khat)
+    wl.q_idx[:] = np.round(wl.q_idx)
+    wl.w_idx[:] = 0.5
+    _decode_check(wl, gpu)
+
+
+def test_decode_wave_rows_all_tied(gpu):
+    # every score +0: the lowest K indices
+    wl = workload.decode_workload(631, [8192, 5003], kv_dtype="fp8", topk_groups=1024)
+    wl.w_idx[:] = 0.0
+    _decode_check(wl, gpu)
+
+
+def test_decode_wave_rows_odd_stride(gpu):
+    # a score row stride that is not a multiple of 4 (scalar loads), rows
+    # at, just above and well above K groups
+    wl = workload.decode_workload(632, [4 * 2001 + 3, 4 * 512, 4 * 513 + 1, 4 * 1500],
+                                  kv_dtype="fp8", topk_groups=512)
+    assert wl.gstride % 4 != 0 and wl.gstride <= 2048
+    _decode_check(wl, gpu)

@@ -273,7 +273,7 @@ def prefill_workload(seed: int, first_pos: int, n_q: int, num_q_heads=16, num_kv
 CONFIG_SEED = 0x51A0
 
 
-def config(i: int, tail: int = 1) -> Workload:
+def config(i: int, tail: int = 1, instance: int = 0) -> Workload:
     """The five workloads of the QSA layer step (1-based index).
 
     1  decode, 1 request, L = 8,192 + tail (tail 1..3), BF16 KV,
@@ -288,8 +288,11 @@ def config(i: int, tail: int = 1) -> Workload:
     5  decode with shared selection, 4 requests, L0 = 131,072 + r0
        (r0 = 1, 2, 3, 1), 3 positions (base + 2 drafts), Hq 24 / Hkv 2,
        FP8 KV, random pages, K = 1,024.
+
+    instance > 0 gives further independent input sets of the same workload
+    (other seeds), for timing loops that rotate over several.
     """
-    seed = CONFIG_SEED + i
+    seed = CONFIG_SEED + i + 1000 * instance
     if i == 1:
         return decode_workload(seed, [8192 + tail], kv_dtype="bf16", random_pages=False,
                                topk_groups=512, note=f"cfg1 L=8192+{tail}")
