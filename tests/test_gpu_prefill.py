@@ -129,3 +129,13 @@ def test_prefill_head_shapes(gpu, hq, hkv, n_q, kv):
     wl = workload.prefill_workload(840 + 7 * hq + hkv + n_q, 2500, n_q, num_q_heads=hq,
                                    num_kv_heads=hkv, kv_dtype=kv, topk_groups=512)
     _prefill_check(wl, gpu, np.arange(n_q))
+
+
+@pytest.mark.parametrize("first_pos,n_q,K,kv", [
+    (4096, 1024, 1024, "bf16"),    # rows of <= 2,048 groups: one wavefront per row
+    (24576, 2048, 2048, "fp8"),    # 2,049..8,192 groups: the 256-thread pruned top-K
+    (40960, 1024, 1024, "fp8"),    # 8,193..16,384 groups: the 1,024-thread finish kernel
+])
+def test_prefill_topk_paths_and_budgets(gpu, first_pos, n_q, K, kv):
+    wl = workload.prefill_workload(840 + K, first_pos, n_q, kv_dtype=kv, topk_groups=K)
+    _prefill_check(wl, gpu, _sample_rows(wl.n_q, 6))
