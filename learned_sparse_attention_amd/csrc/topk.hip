@@ -7,9 +7,19 @@
 // ranks by (score descending, group index ascending).  Output per row: the
 // min(K, G) selected group ids in ascending order, then -1.
 //
-// Rows longer than kDirect groups (decode at long context: up to 65,536
-// groups per row, only a handful of rows) are spread over many compute
-// units in two launches:
+// Four paths, by the length of the score rows:
+//   up to 2,048 groups (short decode contexts, early prefill queries):
+//            one wavefront per row.  Lane l holds 32 consecutive groups;
+//            the K-th key comes from radix passes over a wave-owned
+//            histogram, the selection from bit masks and wave scans.
+//   up to 8,192 groups (a prefill chunk's thousands of rows): one
+//            256-thread workgroup per row (row kernel).  The row is pruned
+//            with a sampled guess (below) inside the workgroup and only the
+//            candidates are ranked.
+//   up to 16,384 groups (a few decode rows): the row kernel with 512
+//            threads.
+//   longer (decode at long context: up to 65,536 groups per row, a handful
+//            of rows): spread over many compute units in two launches.
 //   extract  one workgroup per 4,096-group slice.  Every slice of a row
 //            derives the same pruning threshold ("guess") from 512 evenly
 //            spaced sample scores of the row: an exact radix select of the
@@ -17,24 +27,16 @@
 //            standard deviations of its sampling error, so the guess lies
 //            below the K-th largest score with overwhelming probability.
 //            The slice then writes every score >= guess (typically ~6.6% at
-//            K/G = 1/32) with its index to its own region of the workspace.
+//            K/G = 1/32) with its index to its own region of the workspace,
+//            and records its count, its largest key and the guess.
 //   finish   one workgroup per row gathers the candidates (~4K), finds the
-//            K-th key T exactly with four 8-bit radix passes over the key
-//            offsets from the smallest candidate, marks key > T and key == T
-//            in LDS bitmaps, and emits ascending indices, copies of T in
-//            index order, through a block scan of bitmap popcounts.
-//            If a slice overflowed or fewer than K candidates survived (the
-//            guess missed), the row is re-ranked exactly from the full score
-//            row instead, so the result never depends on the sample.
-// Rows of up to 2,048 groups (short decode contexts, early prefill queries)
-// take one wavefront each: lane l holds 32 consecutive groups, the K-th key
-// comes from radix passes over a wave-owned histogram and the selection
-// from bit masks and wave scans.
-// Short rows (up to 8,192 groups: prefill queries, thousands of rows) take
-// one 256-thread workgroup each (row kernel): the row is pruned with the
-// same sampled guess inside the workgroup and only the candidates are
-// ranked.  Rows of 8,193 to 16,384 groups (a few decode rows) go straight
-// to the finish step with every group a candidate.
+//            K-th key T exactly with radix passes of up to 12 bits over the
+//            key offsets from the guess, marks key > T and key == T in LDS
+//            bitmaps, and emits ascending indices, copies of T in index
+//            order, through a block scan of bitmap popcounts.
+// Whenever a guess misses (a slice or a wave's candidate region overflows,
+// or fewer than K candidates survive), the row is ranked exactly from all of
+// its scores instead, so the result never depends on the sample.
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
@@ -200,51 +202,6 @@ __device__ uint32_t wave_select_span(const uint32_t (&k)[M], uint32_t r, uint32_
     pmask |= dmask << s;
     nbits = s;
   }
-  return kmin + prefix;
-}
-
-// Exact threshold among M candidate keys per thread (0 = empty slot):
-// the need-th largest key T and how many copies of T are taken.  Radix
-// passes of 8 bits over the offsets key - kmin, starting at the highest
-// bit where the candidates differ.
-template <int NT, int M>
-__device__ uint32_t candidate_threshold(const uint32_t (&key)[M], uint32_t need, uint32_t* hist,
-                                        uint32_t* tmp, int* sh, uint32_t* take_eq) {
-  constexpr int NW = NT / kWave;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    if (key[m]) { kmin = min(kmin, key[m]); kmax = max(kmax, key[m]); }
-  }
-  kmin = wave_min_u32(kmin);
-  kmax = wave_max_u32(kmax);
-  if (lane == 0) { tmp[wid] = kmin; tmp[NW + wid] = kmax; }
-  __syncthreads();
-  kmin = tmp[0]; kmax = tmp[NW];
-  for (int w = 1; w < NW; ++w) { kmin = min(kmin, tmp[w]); kmax = max(kmax, tmp[NW + w]); }
-  __syncthreads();
-  const uint32_t span = kmax - kmin;
-  int nbits = span ? 32 - __clz(span) : 0;  // offsets fit in nbits bits
-  uint32_t prefix = 0, pmask = 0;           // over offsets
-  while (nbits > 0) {
-    const int s = nbits > 8 ? nbits - 8 : 0;
-    const uint32_t dmask = (1u << (nbits - s)) - 1u;
-    for (int i = tid; i < 256; i += NT) hist[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const uint32_t off = key[m] - kmin;
-      if (key[m] && (off & pmask) == prefix) atomicAdd(&hist[(off >> s) & dmask], 1u);
-    }
-    __syncthreads();
-    uint32_t d;
-    block_find256(hist, need, sh, &d, &need);
-    prefix |= d << s;
-    pmask |= dmask << s;
-    nbits = s;
-  }
-  *take_eq = need;
   return kmin + prefix;
 }
 
@@ -685,18 +642,18 @@ __global__ __launch_bounds__(kExtractThreads) void topk_extract_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// finish: one workgroup per row
+// finish: one workgroup per long row, over the candidates its slices kept
 
-template <bool kFromCand, int MC, int NT, int kMaxG>
-__global__ __launch_bounds__(NT) void topk_finish_kernel(
+__global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     const float* __restrict__ scores, int gstride, const int32_t* __restrict__ row_len,
     int first_pos, int max_ctx, int K, const uint32_t* __restrict__ cand_val,
     const uint16_t* __restrict__ cand_idx, const int32_t* __restrict__ cand_cnt,
     int32_t* __restrict__ out) {
-  constexpr int NW = NT / kWave;
-  constexpr int kW = kMaxG / 32 > NT ? kMaxG / 32 : NT;  // bitmap words (at least one per thread)
-  // the value-linear bins serve only the re-ranking of candidate rows
-  __shared__ __attribute__((aligned(16))) uint32_t hist[kFromCand ? kBins : 256];
+  constexpr int NT = kFinishThreads, NW = NT / kWave;
+  constexpr int MC = kMaxSlices;        // slot row m of thread t: slice m, slot t
+  constexpr int kW = kMaxGroups / 32;   // bitmap words
+  static_assert(kSliceCap == NT, "one slice per slot row");
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
   __shared__ uint32_t selmap[kW];
   __shared__ uint32_t eqmap[kW];
   __shared__ uint32_t tmp[2 * NW + 1];
@@ -705,27 +662,21 @@ __global__ __launch_bounds__(NT) void topk_finish_kernel(
 
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
-  // Candidate slots and counts are fetched first, before the row length is
-  // known (every slot lies inside the workspace), so their latency overlaps
-  // the length load; slot m*NT + tid lies in slice m (kSliceCap == NT).
-  uint32_t ck[MC];
-  uint32_t cg[MC];
+  // Candidate slots and the slices' records are fetched first, before the
+  // row length is known (every slot lies inside the workspace), so their
+  // latency overlaps the length load.
+  uint32_t ck[MC], cg[MC], kmx[MC];
   int cnt[MC];
-  uint32_t kmx[MC];
-  uint32_t gk = 0u;  // the guess: every candidate key is >= gk
-  if (kFromCand) {
-    static_assert(!kFromCand || kSliceCap == NT, "one slice per slot row");
-    static_assert(!kFromCand || MC == kMaxSlices, "one count per slot row");
-    const size_t base = (size_t)row * kMaxSlices * kSliceCap;
+  const size_t base = (size_t)row * kMaxSlices * kSliceCap;
 #pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      cnt[m] = cand_cnt[(size_t)(row * kMaxSlices + m) * kInfo];
-      kmx[m] = (uint32_t)cand_cnt[(size_t)(row * kMaxSlices + m) * kInfo + 1];
-      ck[m] = cand_val[base + m * NT + tid];
-      cg[m] = cand_idx[base + m * NT + tid];
-    }
-    gk = (uint32_t)cand_cnt[(size_t)row * kMaxSlices * kInfo + 2];
+  for (int m = 0; m < MC; ++m) {
+    cnt[m] = cand_cnt[(size_t)(row * kMaxSlices + m) * kInfo];
+    kmx[m] = (uint32_t)cand_cnt[(size_t)(row * kMaxSlices + m) * kInfo + 1];
+    ck[m] = cand_val[base + m * NT + tid];
+    cg[m] = cand_idx[base + m * NT + tid];
   }
+  // the guess (slice 0 always derives it): every candidate key is >= gk
+  const uint32_t gk = (uint32_t)cand_cnt[(size_t)row * kMaxSlices * kInfo + 2];
   const int L = row_len ? row_len[row] : first_pos + row + 1;
   int G = (L >= 0 && L <= max_ctx) ? L / kRatio : 0;
   if (G > gstride) G = gstride;
@@ -738,45 +689,30 @@ __global__ __launch_bounds__(NT) void topk_finish_kernel(
   const int nwords = (G + 31) / 32;
   for (int i = tid; i < nwords; i += NT) { selmap[i] = 0u; eqmap[i] = 0u; }
 
-  // candidates: slot m*NT + tid
+  const int n_slices = (G + kSlice - 1) / kSlice;
   bool ok = true;
-  if (kFromCand) {
-    const int n_slices = (G + kSlice - 1) / kSlice;
+  uint32_t C = 0;
 #pragma unroll
-    for (int m = 0; m < MC; ++m) cnt[m] = m < n_slices ? cnt[m] : 0;
-    uint32_t C = 0;
-#pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      ok &= cnt[m] <= kSliceCap;
-      C += (uint32_t)cnt[m];
-    }
-    ok &= C >= (uint32_t)K;
-#pragma unroll
-    for (int m = 0; m < MC; ++m)
-      ck[m] = (ok && tid < cnt[m]) ? score_key(__uint_as_float(ck[m])) : 0u;
-  } else {
-#pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      const int i = m * NT + tid;
-      ck[m] = i < G ? score_key(srow[i]) : 0u;
-      cg[m] = (uint32_t)i;
-    }
+  for (int m = 0; m < MC; ++m) {
+    cnt[m] = m < n_slices ? cnt[m] : 0;
+    ok &= cnt[m] <= kSliceCap;
+    C += (uint32_t)cnt[m];
   }
+  ok &= C >= (uint32_t)K;
   uint32_t T = 0, take_eq = 0;
-  if (!kFromCand || ok) {
-    if constexpr (kFromCand) {
-      uint32_t kmax = 0u;
+  if (ok) {
+    uint32_t kmax = 0u;
 #pragma unroll
-      for (int m = 0; m < MC; ++m) kmax = max(kmax, cnt[m] > 0 ? kmx[m] : 0u);
-      T = wide_threshold<NT, MC>(ck, gk, kmax, (uint32_t)K, hist, sh, &take_eq);
+    for (int m = 0; m < MC; ++m) {
+      ck[m] = tid < cnt[m] ? score_key(__uint_as_float(ck[m])) : 0u;
+      kmax = max(kmax, cnt[m] > 0 ? kmx[m] : 0u);
     }
-    else
-      T = row_threshold<NT, MC>(ck, (uint32_t)K, hist, red, sh, &take_eq);
+    T = wide_threshold<NT, MC>(ck, gk, kmax, (uint32_t)K, hist, sh, &take_eq);
 #pragma unroll
     for (int m = 0; m < MC; ++m)
       if (ck[m] >= T && ck[m]) atomicOr(ck[m] > T ? &selmap[cg[m] >> 5] : &eqmap[cg[m] >> 5],
                                         1u << (cg[m] & 31));
-  } else if constexpr (kFromCand) {
+  } else {
     // the pruning guess missed: exact ranking of the whole row
     T = exact_threshold_stream<NT>(srow, G, (uint32_t)K, hist, red, sh, &take_eq);
     for (int i = tid; i < G; i += NT) {
@@ -833,16 +769,17 @@ __device__ uint32_t pruned_threshold(const uint32_t (&key)[M], int active, uint3
   return kmin + prefix;
 }
 
-template <int NT>
+template <int NT, int kMaxG>
 __global__ __launch_bounds__(NT) void topk_row_kernel(const float* __restrict__ scores,
                                                       int gstride,
                                                       const int32_t* __restrict__ row_len,
                                                       int first_pos, int max_ctx, int K,
                                                       int32_t* __restrict__ out) {
   constexpr int NW = NT / kWave;
-  constexpr int E = kShort / (4 * NT);  // 16-byte chunks per thread
+  constexpr int E = kMaxG / (4 * NT);   // 16-byte chunks per thread
   constexpr int M = 4 * E;              // keys per thread: key 4e + c is group 4 (e NT + t) + c
-  constexpr int kW = kShort / 32 > NT ? kShort / 32 : NT;  // bitmap words
+  constexpr int kW = kMaxG / 32 > NT ? kMaxG / 32 : NT;  // bitmap words
+  static_assert(kMaxG <= 65536 && M <= 32, "16-bit group ids, one mask bit per key");
   constexpr int kCW = kRowCap / NW;     // candidate slots per wave
   constexpr int MC = kRowCap / NT;      // candidate slots per thread
   __shared__ __attribute__((aligned(16))) uint32_t hist[256];
@@ -1058,14 +995,16 @@ hipError_t launch_topk(const float* scores, int gstride, int n_rows, const int32
   }
   if (gstride <= kShort) {
     // many short rows (prefill): small workgroups, several rows per CU
-    hipLaunchKernelGGL((topk_row_kernel<kShortThreads>), dim3(n_rows), dim3(kShortThreads), 0,
-                       stream, scores, gstride, row_len, first_pos, max_ctx, K, out);
+    hipLaunchKernelGGL((topk_row_kernel<kShortThreads, kShort>), dim3(n_rows),
+                       dim3(kShortThreads), 0, stream, scores, gstride, row_len, first_pos, max_ctx,
+                       K, out);
     return hipGetLastError();
   }
   if (gstride <= kDirect) {
-    hipLaunchKernelGGL((topk_finish_kernel<false, kDirect / kFinishThreads, kFinishThreads, kDirect>),
-                       dim3(n_rows), dim3(kFinishThreads), 0, stream, scores, gstride, row_len,
-                       first_pos, max_ctx, K, nullptr, nullptr, nullptr, out);
+    // a few longer rows: twice the threads, the same 32 keys each
+    hipLaunchKernelGGL((topk_row_kernel<2 * kShortThreads, kDirect>), dim3(n_rows),
+                       dim3(2 * kShortThreads), 0, stream, scores, gstride, row_len, first_pos,
+                       max_ctx, K, out);
     return hipGetLastError();
   }
   if (!ws) return hipErrorInvalidValue;
@@ -1082,8 +1021,7 @@ hipError_t launch_topk(const float* scores, int gstride, int n_rows, const int32
                      samples);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((topk_finish_kernel<true, kMaxSlices * kSliceCap / kFinishThreads,
-                                          kFinishThreads, kMaxGroups>),
+  hipLaunchKernelGGL(topk_finish_kernel,
                      dim3(n_rows), dim3(kFinishThreads), 0, stream, scores, gstride, row_len,
                      first_pos, max_ctx, K, cval, cidx, ccnt, out);
   return hipGetLastError();

@@ -274,3 +274,30 @@ def test_decode_wave_rows_odd_stride(gpu):
                                   kv_dtype="fp8", topk_groups=512)
     assert wl.gstride % 4 != 0 and wl.gstride <= 2048
     _decode_check(wl, gpu)
+
+
+# Rows of 8,193 to 16,384 groups: the pruned row kernel with 512 threads.
+
+def test_decode_16k_rows_sample_miss(gpu):
+    # the sample positions are the top scorers: the guess keeps ~100
+    # candidates for K = 1,024 and the whole-row ranking takes over
+    wl = workload.decode_workload(640, [65536, 40001], kv_dtype="fp8", topk_groups=1024)
+    gpp = 16
+    for b, L in enumerate(wl.ctx_lens):
+        G = int(L) // 4
+        for i in range(512):
+            g = (i * G) // 512
+            wl.khat[wl.page_table[b, g // gpp], g % gpp] = 4.0 * wl.q_idx[b]
+    _decode_check(wl, gpu)
+
+
+def test_decode_16k_rows_ties_and_pruned(gpu):
+    # coarse scores (tie runs at the K-th score) on one row, all scores +0
+    # (overflowing candidate regions) on another, normal scores on a third
+    wl = workload.decode_workload(641, [65536, 50000, 36001], kv_dtype="bf16", topk_groups=2048)
+    for b in (0,):
+        pages = wl.page_table[b, :(int(wl.ctx_lens[b]) + 63) // 64]
+        wl.khat[pages] = np.round(wl.khat[pages])
+    wl.q_idx[0] = np.round(wl.q_idx[0])
+    wl.w_idx[1] = 0.0
+    _decode_check(wl, gpu)
