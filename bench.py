@@ -19,6 +19,7 @@ baseline.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -416,6 +417,11 @@ def main() -> int:
     t0 = time.perf_counter()
     wls = [workload.config(args.config, instance=k) for k in range(n_sets)]
     t_gen = time.perf_counter() - t0
+    # A collector pass inside a timed loop (the binding allocates small host
+    # objects per call) would stall the launches for milliseconds: collect
+    # now and keep the collector off until the GPU legs are done.
+    gc.collect()
+    gc.disable()
     devs = [H.to_dev(w, dev) for w in wls]
     wl, d = wls[0], devs[0]
     g = wl.geom
@@ -524,6 +530,7 @@ def main() -> int:
         result["mqa_indexer"] = mqa_indexer(dev, max(10, args.steps // 2), 3)
     if args.calibrate_copy:
         calibrate_copy(dev)
+    gc.enable()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result))

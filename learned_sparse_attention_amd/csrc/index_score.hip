@@ -25,17 +25,17 @@
 namespace qsa {
 namespace {
 
-constexpr int kScoreThreads = 256;  // 4 waves, one k̂ page each per step
-// Pages per wavefront: two when the launch has pages to spare, one when it
-// is small (a single short request), so each wave's chain of dependent
-// loads is as short as possible.
-constexpr int kSmallLaunchPages = 8192;
+constexpr int kScoreThreads = 256;  // 4 waves, one k̂ page each
+// One page per wavefront: the grid (8 rows x 4,096 pages = 8,192
+// workgroups at the longest context) drains in finer steps than with two
+// pages per wave, and each wave's chain of dependent loads (row length,
+// page id, k̂) is paid once.
+constexpr int kPagesPerWave = 1;
 
 __device__ __forceinline__ float dot4(float4 a, float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
 
-template <int PPW>
 __global__ __launch_bounds__(kScoreThreads) void index_score_gemv_kernel(
     const float* __restrict__ khat, const int32_t* __restrict__ page_table, int max_pages,
     int num_pages, const int32_t* __restrict__ row_req, const int32_t* __restrict__ row_len,
@@ -63,8 +63,8 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_gemv_kernel(
   const int row_pages = (gstride + kGroupsPerPage - 1) / kGroupsPerPage;
   const int* pt = page_table + (size_t)req * max_pages;
 
-  for (int i = 0; i < PPW; ++i) {
-    const int page = blockIdx.x * 4 * PPW + i * 4 + wave;
+  for (int i = 0; i < kPagesPerWave; ++i) {
+    const int page = blockIdx.x * 4 * kPagesPerWave + i * 4 + wave;
     if (page >= row_pages) break;
     const int g0 = page * kGroupsPerPage;
     float sc = -INFINITY;
@@ -115,7 +115,6 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_gemv_kernel(
 // shuffle within the half-wave.
 constexpr int kMqaHeads = 4, kMqaDim = 128;
 
-template <int PPW>
 __global__ __launch_bounds__(kScoreThreads) void index_score_gemv_mqa_kernel(
     const float* __restrict__ khat, const int32_t* __restrict__ page_table, int max_pages,
     int num_pages, const int32_t* __restrict__ row_req, const int32_t* __restrict__ row_len,
@@ -144,8 +143,8 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_gemv_mqa_kernel(
   const int row_pages = (gstride + kGroupsPerPage - 1) / kGroupsPerPage;
   const int* pt = page_table + (size_t)req * max_pages;
 
-  for (int i = 0; i < PPW; ++i) {
-    const int page = blockIdx.x * 4 * PPW + i * 4 + wave;
+  for (int i = 0; i < kPagesPerWave; ++i) {
+    const int page = blockIdx.x * 4 * kPagesPerWave + i * 4 + wave;
     if (page >= row_pages) break;
     const int g0 = page * kGroupsPerPage;
     float sc = -INFINITY;
@@ -197,11 +196,8 @@ hipError_t launch_index_score_gemv(const float* khat, const int32_t* page_table,
                                    bool shared_key) {
   if (n_rows <= 0 || gstride <= 0) return hipSuccess;
   const int row_pages = (gstride + kGroupsPerPage - 1) / kGroupsPerPage;
-  const bool small = (long long)n_rows * row_pages < kSmallLaunchPages;
-  const int ppw = small ? 1 : 2;
-  dim3 grid((row_pages + 4 * ppw - 1) / (4 * ppw), n_rows, 1);
-  auto kern = shared_key ? (small ? index_score_gemv_mqa_kernel<1> : index_score_gemv_mqa_kernel<2>)
-                         : (small ? index_score_gemv_kernel<1> : index_score_gemv_kernel<2>);
+  dim3 grid((row_pages + 4 * kPagesPerWave - 1) / (4 * kPagesPerWave), n_rows, 1);
+  auto kern = shared_key ? index_score_gemv_mqa_kernel : index_score_gemv_kernel;
   hipLaunchKernelGGL(kern, grid, dim3(kScoreThreads), 0, stream, khat,
                      page_table, max_pages, num_pages, row_req, row_len, req0, first_pos, max_ctx,
                      q_idx, w_idx, scores, gstride, samples);
