@@ -25,11 +25,12 @@
 namespace qsa {
 namespace {
 
-constexpr int kScoreThreads = 256;  // 4 waves, one k̂ page each
-// One page per wavefront: the grid (8 rows x 4,096 pages = 8,192
-// workgroups at the longest context) drains in finer steps than with two
-// pages per wave, and each wave's chain of dependent loads (row length,
-// page id, k̂) is paid once.
+constexpr int kScoreThreads = 128;  // 2 waves, one k̂ page each
+constexpr int kScoreWaves = kScoreThreads / kWave;
+// One page per wavefront and two wavefronts per workgroup: the grid (8 rows
+// x 4,096 pages = 16,384 workgroups at the longest context) drains in fine
+// steps, and each wave's chain of dependent loads (row length, page id, k̂)
+// is paid once.
 constexpr int kPagesPerWave = 1;
 
 __device__ __forceinline__ float dot4(float4 a, float4 b) {
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_gemv_kernel(
   const int* pt = page_table + (size_t)req * max_pages;
 
   for (int i = 0; i < kPagesPerWave; ++i) {
-    const int page = blockIdx.x * 4 * kPagesPerWave + i * 4 + wave;
+    const int page = blockIdx.x * kScoreWaves * kPagesPerWave + i * kScoreWaves + wave;
     if (page >= row_pages) break;
     const int g0 = page * kGroupsPerPage;
     float sc = -INFINITY;
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_gemv_mqa_kernel(
   const int* pt = page_table + (size_t)req * max_pages;
 
   for (int i = 0; i < kPagesPerWave; ++i) {
-    const int page = blockIdx.x * 4 * kPagesPerWave + i * 4 + wave;
+    const int page = blockIdx.x * kScoreWaves * kPagesPerWave + i * kScoreWaves + wave;
     if (page >= row_pages) break;
     const int g0 = page * kGroupsPerPage;
     float sc = -INFINITY;
@@ -196,7 +197,8 @@ hipError_t launch_index_score_gemv(const float* khat, const int32_t* page_table,
                                    bool shared_key) {
   if (n_rows <= 0 || gstride <= 0) return hipSuccess;
   const int row_pages = (gstride + kGroupsPerPage - 1) / kGroupsPerPage;
-  dim3 grid((row_pages + 4 * kPagesPerWave - 1) / (4 * kPagesPerWave), n_rows, 1);
+  const int per_block = kScoreWaves * kPagesPerWave;
+  dim3 grid((row_pages + per_block - 1) / per_block, n_rows, 1);
   auto kern = shared_key ? index_score_gemv_mqa_kernel : index_score_gemv_kernel;
   hipLaunchKernelGGL(kern, grid, dim3(kScoreThreads), 0, stream, khat,
                      page_table, max_pages, num_pages, row_req, row_len, req0, first_pos, max_ctx,
