@@ -301,3 +301,11 @@ def test_decode_16k_rows_ties_and_pruned(gpu):
     wl.q_idx[0] = np.round(wl.q_idx[0])
     wl.w_idx[1] = 0.0
     _decode_check(wl, gpu)
+
+
+@pytest.mark.parametrize("K", [1, 7, 100])
+@pytest.mark.parametrize("lens", [[8000, 6003], [60000, 40003], [200001]],
+                         ids=["wave-rows", "rows-512-threads", "long-rows"])
+def test_decode_small_budgets_each_topk_path(gpu, K, lens):
+    wl = workload.decode_workload(650 + K, lens, kv_dtype="fp8", topk_groups=K)
+    _decode_check(wl, gpu)
