@@ -178,6 +178,89 @@ def write_counters(fetch_dir: str, write_dir: str, workload_name: str, commands:
     print(json.dumps(rec))
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_BUSY_CYCLES",
+                 "GRBM_GUI_ACTIVE")
+PREFILL_SLUG = "prefill_q4096_p28672_g8192"
+N_XCC, N_SIMD = 8, 1024
+
+
+def write_mfma_counters(pmc_dir: str, commands: list) -> None:
+    """Turn one rocprofv3 --pmc run of the four MFMA_COUNTERS into matrix-core
+    utilisation per matrix-core kernel.  rocprofv3 reports GRBM_GUI_ACTIVE
+    summed over the 8 XCDs (it reads 8x the kernel's cycles), so the per-XCD
+    busy time is that sum / 8; utilisation = MFMA busy cycles summed over all
+    SIMDs / (per-XCD GPU-active cycles x 1,024 SIMDs), and flops = MOPS x 512.
+    Writes a text table and profiles/index_score_mfma__<workload>.counters.json."""
+    import csv
+    import glob
+    d = _read_counters(pmc_dir)
+    kernels = sorted({k for (k, c) in d if c == "SQ_VALU_MFMA_BUSY_CYCLES"})
+    # mean dispatch duration (ns) per kernel, to check the XCD reading: the
+    # per-XCD cycles over it must come out near the shader clock
+    durs: dict = {}
+    for fn in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                durs.setdefault(row["Kernel_Name"], {})[row["Dispatch_Id"]] = (
+                    int(row["End_Timestamp"]) - int(row["Start_Timestamp"]))
+    lines = [f"# Matrix-core utilisation per dispatch (rocprofv3 --pmc), prefill chunk of 4,096 "
+             f"queries at positions 28,672..32,767 (8,192 groups)", "",
+             "Command:", *[f"    {c}" for c in commands], "",
+             "util = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1,024 SIMDs); "
+             "GFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / 1e9", "",
+             "GRBM_GUI_ACTIVE is read as the sum over the 8 XCDs: an eighth of it over the "
+             "dispatch's duration (the 'GHz implied' column) comes out at the shader clock for "
+             "the long dispatches; short ones carry the counter window's own overhead.  Each "
+             "16x16x32 BF16 MFMA counts 32 MOPs and 16 busy cycles, so the utilisation is the "
+             "issued flops over the peak at the clock the kernel actually ran at.", "",
+             "| kernel | us | GRBM_GUI_ACTIVE (sum of 8 XCDs) | GHz implied | SQ_BUSY_CYCLES | "
+             "MFMA_MOPS_BF16 | MFMA_BUSY_CYCLES | GFLOP | MFMA util |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    recs = {}
+    for k in kernels:
+        grbm = d.get((k, "GRBM_GUI_ACTIVE"))
+        busy = d[(k, "SQ_VALU_MFMA_BUSY_CYCLES")]
+        mops = d.get((k, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), 0.0)
+        if not grbm or not busy:
+            continue
+        util = busy / (grbm / N_XCC * N_SIMD)
+        short = k.replace("qsa::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        dk = durs.get(k, {})
+        us = sum(dk.values()) / len(dk) / 1e3 if dk else float("nan")
+        lines.append(f"| {short[:70]} | {us:.1f} | {grbm:.0f} | {grbm / N_XCC / us / 1e3:.2f} | "
+                     f"{d.get((k, 'SQ_BUSY_CYCLES'), 0):.0f} | {mops:.0f} | {busy:.0f} | "
+                     f"{mops * 512 / 1e9:.2f} | {100 * util:.1f}% |")
+        if "index_score_mfma_kernel" in short:
+            recs[short.split("<", 1)[1].rsplit(">", 1)[0].strip()] = {
+                "mfma_util": util, "flops_per_launch": mops * 512, "us_per_launch": us,
+                "grbm_gui_active_sum": grbm, "mfma_busy_cycles": busy}
+    with open(os.path.join(ROOT, "profiles", f"mfma_util__{PREFILL_SLUG}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    rec = {"kernel": "index_score_mfma_kernel", "workload": PREFILL_SLUG,
+           "source_digest": source_digest("index_score_prefill.hip", "qsa_device.h"),
+           "forms": recs, "commands": commands}
+    with open(os.path.join(ROOT, "profiles",
+                           f"index_score_mfma__{PREFILL_SLUG}.counters.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
+def measured_mfma_util(form: str):
+    """Matrix-core utilisation of index_score_mfma_kernel<form> from the
+    committed counter summary, if it was taken on the current kernel source;
+    else None."""
+    path = os.path.join(ROOT, "profiles", f"index_score_mfma__{PREFILL_SLUG}.counters.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_digest") != source_digest("index_score_prefill.hip", "qsa_device.h"):
+        return None
+    return d.get("forms", {}).get(form, {}).get("mfma_util")
+
+
 def prefill_scoring(dev, steps: int, warmup: int) -> dict:
     """The long-prefill chunk (4,096 queries at positions 28,672 .. 32,767 of
     one request, 8,192 groups): the matrix-core indexer scoring alone, timed
@@ -235,6 +318,7 @@ def prefill_scoring(dev, steps: int, warmup: int) -> dict:
             "frac_vs_fp32_mfma_peak": tflops / FP32_MFMA_PEAK_TFLOPS,
             "flops_per_launch": visible, "dense_tile_flops": dense, "ms_per_launch": ms,
             "score_bytes_written": wl.n_q * gstride * 4,
+            "mfma_util_counters": measured_mfma_util("Form<8, 8, 64>"),
             "prefill_step_ms": ms_step}
 
 
@@ -305,7 +389,8 @@ def mqa_indexer(dev, steps: int, warmup: int) -> dict:
                                 "kernel": "index_score_mfma_kernel<SharedKeyForm>",
                                 "achieved": tflops, "peak": BF16_PEAK_TFLOPS,
                                 "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS,
-                                "flops_per_launch": visible, "ms_per_launch": ms_pf}}
+                                "flops_per_launch": visible, "ms_per_launch": ms_pf,
+                                "mfma_util_counters": measured_mfma_util("Form<4, 1, 128>")}}
 
 
 def kv_append(dev, steps: int, warmup: int) -> dict:
@@ -392,9 +477,15 @@ def main() -> int:
                     help="also launch a 1 GiB copy kernel (for counter runs)")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: summarise two rocprofv3 --pmc runs into profiles/")
+    ap.add_argument("--write-mfma-counters", metavar="PMC_DIR",
+                    help="no GPU: summarise a rocprofv3 --pmc run of the matrix-core counters "
+                         "into profiles/")
     ap.add_argument("--counter-commands", nargs="*", default=[],
                     help="the commands that made the counter runs (recorded with them)")
     args = ap.parse_args()
+    if args.write_mfma_counters:
+        write_mfma_counters(args.write_mfma_counters, args.counter_commands)
+        return 0
     if args.write_counters:
         write_counters(*args.write_counters, WORKLOAD_SLUG[args.config], args.counter_commands)
         return 0
