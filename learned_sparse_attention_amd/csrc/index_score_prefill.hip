@@ -288,13 +288,22 @@ __global__ __launch_bounds__(kPfThreads, 1) void index_score_mfma_kernel(
       // VGPRs each).  ReLU is an integer max on the bit pattern (negative
       // floats are negative integers; -0 becomes +0).
       const u32x4* kb = lds + buf * kKBlockSlots + hf * kKPitch + ql;
+      // with one key head (multi-query form) all heads share the A
+      // operands: they are read from LDS once per block
+      constexpr bool kShared = F::kHk == 1;
+      u32x4 ash[kShared ? kS : 1];
+      if (kShared) {
+#pragma unroll
+        for (int s = 0; s < kS; ++s) ash[s] = kb[s * 2 * kKPitch];
+      }
       auto head = [&](int h) {
         f32x16 acc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
 #pragma unroll
         for (int s = 0; s < kS; ++s) {
-          const u32x4 a = kb[((h * F::kHk / kH) * kS + s) * 2 * kKPitch];
+          const u32x4 a = kShared ? ash[kShared ? s : 0]
+                                  : kb[((h * F::kHk / kH) * kS + s) * 2 * kKPitch];
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                         __builtin_bit_cast(bf16x8, qb[h][s]), acc,
                                                         0, 0, 0);
