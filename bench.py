@@ -85,10 +85,11 @@ def source_digest(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str, digest: str):
+def measured_traffic(kernel: str, workload: str, digest: str, profiles_dir: str = None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.counters.json")
+    path = os.path.join(profiles_dir or os.path.join(ROOT, "profiles"),
+                        f"{kernel}__{workload}.counters.json")
     try:
         with open(path) as f:
             d = json.load(f)
@@ -132,7 +133,8 @@ def _read_counters(path: str) -> dict:
     return {k: v[0] / v[1] for k, v in sums.items()}
 
 
-def write_counters(fetch_dir: str, write_dir: str, workload_name: str, commands: list) -> None:
+def write_counters(fetch_dir: str, write_dir: str, workload_name: str, commands: list,
+                   out_dir: str = None) -> None:
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
     dispatch) into HBM bytes per launch, each scaled by what the counter reads
     for the calibration copy; writes profiles/<kernel>__<workload>.counters.json
@@ -161,8 +163,9 @@ def write_counters(fetch_dir: str, write_dir: str, workload_name: str, commands:
         tot = f_ * 1024.0 * ff + w_ * 1024.0 * fw
         short = k.replace("qsa::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
         lines.append(f"| {short[:90]} | {f_:.0f} | {w_:.0f} | {tot:.0f} |")
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", f"hbm_traffic__{workload_name}.md"), "w") as f:
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, f"hbm_traffic__{workload_name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     sf = mean(fetch, "index_score_gemv_kernel", "FETCH_SIZE")
     sw = mean(write, "index_score_gemv_kernel", "WRITE_SIZE")
@@ -171,8 +174,7 @@ def write_counters(fetch_dir: str, write_dir: str, workload_name: str, commands:
            "fetch_kib": sf, "write_kib": sw, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
            "fetch_factor": ff, "write_factor": fw,
            "hbm_bytes_per_launch": sf * 1024.0 * ff + sw * 1024.0 * fw, "commands": commands}
-    with open(os.path.join(ROOT, "profiles",
-                           f"index_score_gemv__{workload_name}.counters.json"), "w") as f:
+    with open(os.path.join(out_dir, f"index_score_gemv__{workload_name}.counters.json"), "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec))
@@ -184,7 +186,7 @@ PREFILL_SLUG = "prefill_q4096_p28672_g8192"
 N_XCC, N_SIMD = 8, 1024
 
 
-def write_mfma_counters(pmc_dir: str, commands: list) -> None:
+def write_mfma_counters(pmc_dir: str, commands: list, out_dir: str = None) -> None:
     """Turn one rocprofv3 --pmc run of the four MFMA_COUNTERS into matrix-core
     utilisation per matrix-core kernel.  rocprofv3 reports GRBM_GUI_ACTIVE
     summed over the 8 XCDs (it reads 8x the kernel's cycles), so the per-XCD
@@ -234,23 +236,25 @@ def write_mfma_counters(pmc_dir: str, commands: list) -> None:
             recs[short.split("<", 1)[1].rsplit(">", 1)[0].strip()] = {
                 "mfma_util": util, "flops_per_launch": mops * 512, "us_per_launch": us,
                 "grbm_gui_active_sum": grbm, "mfma_busy_cycles": busy}
-    with open(os.path.join(ROOT, "profiles", f"mfma_util__{PREFILL_SLUG}.md"), "w") as f:
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, f"mfma_util__{PREFILL_SLUG}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     rec = {"kernel": "index_score_mfma_kernel", "workload": PREFILL_SLUG,
            "source_digest": source_digest("index_score_prefill.hip", "qsa_device.h"),
            "forms": recs, "commands": commands}
-    with open(os.path.join(ROOT, "profiles",
-                           f"index_score_mfma__{PREFILL_SLUG}.counters.json"), "w") as f:
+    with open(os.path.join(out_dir, f"index_score_mfma__{PREFILL_SLUG}.counters.json"), "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec))
 
 
-def measured_mfma_util(form: str):
+def measured_mfma_util(form: str, profiles_dir: str = None):
     """Matrix-core utilisation of index_score_mfma_kernel<form> from the
     committed counter summary, if it was taken on the current kernel source;
     else None."""
-    path = os.path.join(ROOT, "profiles", f"index_score_mfma__{PREFILL_SLUG}.counters.json")
+    path = os.path.join(profiles_dir or os.path.join(ROOT, "profiles"),
+                        f"index_score_mfma__{PREFILL_SLUG}.counters.json")
     try:
         with open(path) as f:
             d = json.load(f)
