@@ -18,10 +18,14 @@
  *      sharing one key (kh(h) = 0); all inputs fp32.
  *   2. Exact top-K.  Among the complete groups g < floor(L/4) (L = tokens
  *      including the current one) keep the K = topk_groups highest scores,
- *      ranking by (score descending, group index ascending); K is a group
- *      budget of 512, 1024 or 2048 at ratio 4 (TRT-LLM config,
- *      enable_heuristic_topk).  If floor(L/4) <= K every complete group is
- *      kept, so the step equals dense causal attention.
+ *      ranking by (score descending, group index ascending); K is the group
+ *      budget topk_groups, any value in 1..2048.  The pages' budgets are
+ *      512, 1024 and 2048 groups at ratio 4; the TRT-LLM config
+ *      (enable_heuristic_topk) names that set only as a prerequisite of
+ *      its heuristic Guess-Verify-Refine selector, and otherwise falls back
+ *      to the exact radix top-K, which this library always computes and
+ *      which has no such limit.  If floor(L/4) <= K every complete group
+ *      is kept, so the step equals dense causal attention.
  *   3. Expansion.  Each kept group g becomes tokens 4g..4g+3; the current
  *      partial block [4*floor(L/4), L) of 0..3 tokens is always added.  All
  *      KV stays in the cache; nothing is compressed or evicted (model card,
@@ -78,7 +82,10 @@ enum qsa_kv_dtype {
 
 /* Layer geometry.  The supported values follow the pages' configurations:
  * head_dim 256, page_size 64, compress_ratio 4 (C4), a group budget
- * topk_groups in [1, 2048] (the pages use 512, 1024 and 2048), any GQA
+ * topk_groups in [1, 2048] (the pages use 512, 1024 and 2048; the TRT-LLM
+ * QSASparseAttentionConfig reference, enable_heuristic_topk, requires that
+ * set only for its heuristic GVR selector, not for the exact top-K; values
+ * outside [1, 2048] are refused as QSA_ERR_UNSUPPORTED), any GQA
  * ratio num_q_heads / num_kv_heads with (num_q_heads / num_kv_heads) *
  * q_per_req <= 64 query rows per KV head, and one of two indexer forms:
  *   - per head: idx_heads 8, idx_dim 64, idx_key_heads 8 (or 0), a key of

@@ -5,20 +5,13 @@ from __future__ import annotations
 import numpy as np
 
 import oracle
+import workload
 
 TIE_REL = 1e-6          # top-K: members may differ only within 1e-6 of the K-th score
 ATOL = {0: 2e-3, 1: 2e-2}  # attention max-abs, BF16 KV / FP8 KV
 
 
-def to_dev(wl, device):
-    import torch
-    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
-    d = dict(
-        k=t(wl.k_cache), v=t(wl.v_cache), khat=t(wl.khat), pt=t(wl.page_table),
-        q_idx=t(wl.q_idx), w_idx=t(wl.w_idx), q=t(wl.q.view(np.int16)),
-        ctx=t(wl.ctx_lens), row_req=t(wl.row_req), row_len=t(wl.row_len),
-    )
-    return d
+to_dev = workload.to_device
 
 
 def run_decode(wl, dev_inputs, **kw):
@@ -47,6 +40,37 @@ def score_bound(wl, rows=None, gstride=None, round_bf16=False) -> np.ndarray:
     return oracle.scores(wl.row_req[sel], wl.row_len[sel], np.abs(wl.q_idx[sel]),
                          np.abs(wl.w_idx[sel]), np.abs(wl.khat), wl.page_table, wl.num_pages, gs,
                          round_bf16_inputs=round_bf16)
+
+
+def score_bound_matmul(wl, rows, gstride, chunk=1024) -> np.ndarray:
+    """The same magnitude as score_bound, sum_h |w_h| sum_d |q_hd k_ghd|,
+    for many rows at once: per-head binary64 matrix products (numpy) of the
+    absolute values, with k̂ gathered in logical group order through the
+    page table (groups on out-of-range pages get 0; their scores are -inf).
+    Rounding the inputs to bf16 changes a magnitude by under 2^-8
+    relative, which the factor 1.01 covers."""
+    rows = np.asarray(rows)
+    Hi, Di = wl.q_idx.shape[1:]
+    Hk = wl.khat.shape[2]
+    gpp = wl.khat.shape[1]
+    out = np.zeros((len(rows), gstride))
+    for req in np.unique(wl.row_req[rows]):
+        idx = np.flatnonzero(wl.row_req[rows] == req)
+        npg = min(wl.page_table.shape[1], (gstride + gpp - 1) // gpp)
+        pages = wl.page_table[req, :npg]
+        ok = (pages >= 0) & (pages < wl.num_pages)
+        kabs = np.zeros((npg, gpp, Hk, Di))
+        kabs[ok] = np.abs(wl.khat[pages[ok]])
+        kabs = kabs.reshape(npg * gpp, Hk, Di)[:gstride]
+        for c0 in range(0, len(idx), chunk):
+            sel = idx[c0:c0 + chunk]
+            q = np.abs(wl.q_idx[rows[sel]].astype(np.float64))
+            w = np.abs(wl.w_idx[rows[sel]].astype(np.float64))
+            acc = np.zeros((len(sel), kabs.shape[0]))
+            for h in range(Hi):
+                acc += w[:, h:h + 1] * (q[:, h, :] @ kabs[:, h * Hk // Hi, :].T)
+            out[sel, :kabs.shape[0]] = acc
+    return 1.01 * out
 
 
 def check_scores(gpu_scores: np.ndarray, ora_scores: np.ndarray, G: np.ndarray,

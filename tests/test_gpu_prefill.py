@@ -2,7 +2,9 @@
 through qsa_index_score_prefill, and inside qsa_prefill) against the oracle
 on bf16-rounded indexer inputs, at small ragged sizes that span several
 256-query x 32-group tiles with partial ones, and at the long-prefill chunk
-(4,096 queries at positions 28,672 .. 32,767) on sampled query rows."""
+(4,096 queries at positions 28,672 .. 32,767), the operator suite's
+7,810-query case and chunks past 65,536 tokens: scores and top-K on every
+query row, attention on sampled rows."""
 import numpy as np
 import pytest
 
@@ -74,41 +76,58 @@ def _sample_rows(n_q, seed):
     return np.array(sorted(set(r for r in fixed + extra if 0 <= r < n_q)))
 
 
-def _prefill_check(wl, gpu, rows):
-    """qsa_prefill on the whole chunk; scores, top-K, token lists and
-    attention compared with the oracle on `rows`; the -inf mask on every
-    row; every output finite."""
+def _prefill_check(wl, gpu, attn_rows, score_rows=None):
+    """qsa_prefill on the whole chunk.  Scores and the exact top-K are
+    compared with the oracle on `score_rows` (default: every query row),
+    token lists on those rows, attention on `attn_rows` (the oracle's
+    fp64 attention is the expensive part); the -inf mask and finiteness of
+    the outputs on every row fetched."""
     import torch
     d = H.to_dev(wl, gpu)
     res = H.run_prefill(wl, d)
     torch.cuda.synchronize()
-    r = oracle.prefill(wl, rows=rows)
-    gs = res["scores"].cpu().numpy()
-    G = (wl.row_len[rows] // 4).astype(np.int32)
-    gstride = (wl.first_pos + wl.n_q) // 4
-    H.check_scores(gs[rows], r["scores"], G,
-                   H.score_bound(wl, rows=rows, gstride=gstride, round_bf16=True))
-    gg = res["groups"].cpu().numpy()[rows]
     K = wl.geom["topk_groups"]
-    H.check_topk(gg, gs[rows], r["groups"], r["scores"], G, K)
-    gt = res["tokens"].cpu().numpy()[rows]
+    gstride = (wl.first_pos + wl.n_q) // 4
+    all_rows = score_rows is None
+    rows = np.arange(wl.n_q) if all_rows else np.asarray(score_rows)
+    if all_rows:
+        gs, gg = res["scores"].cpu().numpy(), res["groups"].cpu().numpy()
+        gt, out = res["tokens"].cpu().numpy(), res["out"].cpu().numpy()
+    else:  # only the checked rows leave the GPU
+        ri = torch.from_numpy(rows).to(gpu)
+        gs, gg = res["scores"][ri].cpu().numpy(), res["groups"][ri].cpu().numpy()
+        gt, out = res["tokens"][ri].cpu().numpy(), res["out"][ri].cpu().numpy()
+    del res, d
+    G = (wl.row_len[rows] // 4).astype(np.int32)
+    ora_s = oracle.scores(wl.row_req[rows], wl.row_len[rows], wl.q_idx[rows], wl.w_idx[rows],
+                          wl.khat, wl.page_table, wl.num_pages, gstride, round_bf16_inputs=True)
+    H.check_scores(gs, ora_s, G, H.score_bound_matmul(wl, rows, gstride))
+    H.check_topk(gg, gs, oracle.topk(ora_s, G, K), ora_s, G, K)
+    del ora_s
     W = oracle.token_width(K)
     for i, p in enumerate(rows):
-        assert np.array_equal(gt[i], oracle.position_tokens(gg[i], int(wl.row_len[p]), 0, W))
-    out = res["out"].cpu().numpy()
+        assert np.array_equal(gt[i], oracle.position_tokens(gg[i], int(wl.row_len[p]), 0, W)), p
     assert np.all(np.isfinite(out))
-    ora_o = oracle.attend(wl.geom, wl.row_req[rows], gt, wl.q[rows], wl.k_cache, wl.v_cache,
-                          wl.page_table, wl.num_pages)
-    H.check_attention(out[rows], ora_o, 0 if wl.geom["kv_dtype"] == 0 else 1)
-    # every row's scores, not only the sampled ones: -inf exactly past G
-    Gall = wl.row_len // 4
-    cols = np.arange(gstride)[None, :]
-    assert np.array_equal(np.isneginf(gs), cols >= Gall[:, None])
+    # attention on the GPU's own selection, on the sampled rows
+    pos = {int(p): i for i, p in enumerate(rows)}
+    ai = np.array([pos[int(p)] for p in attn_rows])
+    ora_o = oracle.attend(wl.geom, wl.row_req[attn_rows], gt[ai], wl.q[attn_rows], wl.k_cache,
+                          wl.v_cache, wl.page_table, wl.num_pages)
+    H.check_attention(out[ai], ora_o, 0 if wl.geom["kv_dtype"] == 0 else 1)
+    # -inf exactly past each row's complete groups and on groups whose page
+    # id is out of range
+    cols = np.arange(gstride)
+    pages = wl.page_table[wl.req][np.minimum(cols // 16, wl.page_table.shape[1] - 1)]
+    bad = (pages < 0) | (pages >= wl.num_pages)
+    want = (cols[None, :] >= (wl.row_len[rows] // 4)[:, None]) | bad[None, :]
+    assert np.array_equal(np.isneginf(gs), want)
+    return gs, gg
 
 
-def test_prefill_long_chunk_sampled(gpu):
+def test_prefill_long_chunk_every_row(gpu):
     # the long-prefill chunk at full size, in the launch configuration the
-    # benchmark times; checked on sampled query rows the oracle computes
+    # benchmark times: scores and top-K on every one of the 4,096 query
+    # rows, attention on sampled rows
     wl = workload.config(4)
     _prefill_check(wl, gpu, _sample_rows(wl.n_q, 4))
 
@@ -116,10 +135,73 @@ def test_prefill_long_chunk_sampled(gpu):
 def test_prefill_long_7810_queries_over_65536(gpu):
     # the operator suite's long-prefill case (PR #41855 article, Tests):
     # 7,810 queries ending a 65,536-token cache, 2,051 selected slots each
-    # (K = 512 groups plus the current block), on sampled rows
+    # (K = 512 groups plus the current block).  Scores and top-K on every
+    # row; attention on sampled rows, as the article's test samples rows.
+    # The score rows are 16,384 groups long: the 512-thread row kernel.
     wl = workload.prefill_workload(830, 65536 - 7810, 7810, kv_dtype="bf16", topk_groups=512)
-    assert 4 * wl.geom["topk_groups"] + 3 == 2051
+    assert 4 * wl.geom["topk_groups"] + 3 == 2051 and wl.gstride == 16384
     _prefill_check(wl, gpu, _sample_rows(wl.n_q, 5))
+
+
+# Score rows longer than 16,384 groups (prefill past 65,536 tokens, up to
+# the 262,144-token capacity of the qsa-hisparse offload contract) take the
+# two-launch top-K (per-slice extraction, then one workgroup per row).  In
+# prefill it runs without the scoring kernel's sample buffer: the guess is
+# read from the score rows themselves.
+
+def test_prefill_past_65536_tokens_every_row(gpu):
+    wl = workload.prefill_workload(850, 131072, 1024, kv_dtype="fp8", topk_groups=2048)
+    assert (wl.first_pos + wl.n_q) // 4 > 16384
+    _prefill_check(wl, gpu, _sample_rows(wl.n_q, 7))
+
+
+def test_prefill_past_65536_tokens_k512_bf16(gpu):
+    # rows of 15,750 .. 16,749 groups in a 16,750-group stride: the last
+    # slice of each row is partial and some rows leave it empty
+    wl = workload.prefill_workload(851, 63000, 4000, kv_dtype="bf16", topk_groups=512)
+    assert wl.gstride > 16384
+    _prefill_check(wl, gpu, _sample_rows(wl.n_q, 8))
+
+
+def test_prefill_past_65536_tokens_sample_miss(gpu):
+    # every query shares one indexer query, and the groups at the evenly
+    # spaced guess positions of every row score far above the rest: the
+    # guess keeps only those (under K), so each row's exact full-row
+    # ranking must take over
+    wl = workload.prefill_workload(852, 131072, 8, kv_dtype="fp8", topk_groups=2048)
+    wl.q_idx[:] = wl.q_idx[0]
+    wl.w_idx[:] = wl.w_idx[0]
+    hot = set()
+    for L in wl.row_len:
+        G = int(L) // 4
+        hot |= {(i * G) // 512 for i in range(512)}
+    assert len(hot) < 2048
+    for g in hot:
+        wl.khat[wl.page_table[0, g // 16], g % 16] = 4.0 * wl.q_idx[0]
+    _prefill_check(wl, gpu, np.arange(wl.n_q))
+
+
+def test_prefill_past_65536_tokens_all_tied(gpu):
+    # w = 0: every score +0, every slice overflows its candidate area, and
+    # each row must keep its lowest K group indices
+    wl = workload.prefill_workload(853, 131072, 64, kv_dtype="fp8", topk_groups=2048)
+    wl.w_idx[:] = 0.0
+    _, gg = _prefill_check(wl, gpu, np.array([0, 31, 63]))
+    assert np.array_equal(gg, np.tile(np.arange(2048, dtype=np.int32), (64, 1)))
+
+
+def test_prefill_rows_of_every_length_past_16384_groups(gpu):
+    # one chunk of 65,540 queries from position 0: its score stride is
+    # 16,385 groups, so every row takes the two-launch top-K while the rows
+    # hold anywhere from 0 to 16,385 groups (rows at or under K = 512
+    # groups keep all of them; under 512 groups the guess repeats
+    # positions).  Checked on sampled rows, which alone are copied back.
+    wl = workload.prefill_workload(854, 0, 65540, kv_dtype="fp8", topk_groups=512)
+    assert wl.gstride == 16385
+    rows = np.array(sorted({0, 1, 2, 3, 4, 7, 100, 511, 2047, 2048, 2051, 2052, 4096, 8191,
+                            8192, 12000, 20000, 32767, 40000, 50000, 60000, 65535, 65536,
+                            65537, 65538, 65539}))
+    _prefill_check(wl, gpu, rows[::3], score_rows=rows)
 
 
 @pytest.mark.parametrize("hq,hkv", [(16, 2), (24, 2), (12, 1), (6, 1), (3, 1)])
@@ -132,9 +214,9 @@ def test_prefill_head_shapes(gpu, hq, hkv, n_q, kv):
 
 
 @pytest.mark.parametrize("first_pos,n_q,K,kv", [
-    (4096, 1024, 1024, "bf16"),    # rows of <= 2,048 groups: one wavefront per row
-    (24576, 2048, 2048, "fp8"),    # 2,049..8,192 groups: the 256-thread pruned top-K
-    (40960, 1024, 1024, "fp8"),    # 8,193..16,384 groups: the 1,024-thread finish kernel
+    (4096, 1024, 1024, "bf16"),    # score stride <= 2,048 groups: one wavefront per row
+    (24576, 2048, 2048, "fp8"),    # 2,049..8,192 groups: the 256-thread pruned row kernel
+    (40960, 1024, 1024, "fp8"),    # 8,193..16,384 groups: the 512-thread pruned row kernel
 ])
 def test_prefill_topk_paths_and_budgets(gpu, first_pos, n_q, K, kv):
     wl = workload.prefill_workload(840 + K, first_pos, n_q, kv_dtype=kv, topk_groups=K)

@@ -37,6 +37,12 @@ def test_validate_and_sizes():
                        ("idx_heads", 4), ("idx_dim", 128), ("topk_groups", 4096),
                        ("topk_groups", 0), ("kv_dtype", 7), ("num_kv_heads", 3)):
         assert qsa.validate(dict(g, **{field: bad})) == -2, field
+    # the group budget: any K in 1..2048 (the exact top-K has no further
+    # limit; the set {512, 1024, 2048} binds only a heuristic selector)
+    for K in (1, 3, 511, 512, 777, 1024, 2047, 2048):
+        assert qsa.validate(dict(g, topk_groups=K)) == 0, K
+    for K in (-1, 0, 2049, 4096):
+        assert qsa.validate(dict(g, topk_groups=K)) == -2, K
     # indexer forms: 8 x 64 with a key per head, or 4 x 128 sharing one key
     assert qsa.validate(dict(g, idx_key_heads=0)) == 0
     assert qsa.validate(workload.geometry(indexer="mqa")) == 0

@@ -270,6 +270,20 @@ def prefill_workload(seed: int, first_pos: int, n_q: int, num_q_heads=16, num_kv
                     first_pos=first_pos, n_q=n_q, req=0, note=note)
 
 
+def to_device(wl: Workload, device) -> dict:
+    """Copies of a workload's arrays as torch tensors on `device`, keyed by
+    the names the binding's callers use (marshalling only: the bf16 query
+    bit patterns travel as int16)."""
+    import torch
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    return dict(k=t(wl.k_cache), v=t(wl.v_cache), khat=t(wl.khat), pt=t(wl.page_table),
+                q_idx=t(wl.q_idx), w_idx=t(wl.w_idx), q=t(wl.q.view(np.int16)),
+                ctx=t(wl.ctx_lens), row_req=t(wl.row_req), row_len=t(wl.row_len))
+
+
 CONFIG_SEED = 0x51A0
 
 
