@@ -40,7 +40,8 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers unless a comment says "host".
  *     The caller owns every buffer and the stream; the library allocates
- *     nothing, keeps no pointer after return and holds no global state.
+ *     nothing and keeps no pointer after return.  Its only global state is
+ *     the static scratch area of qsa_decode_noalloc (below).
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
  *     the null stream).  No call synchronises the host or copies device
  *     data to the host, so the calls can be captured into a HIP graph.
@@ -70,7 +71,9 @@ typedef enum qsa_status {
   QSA_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent lengths */
   QSA_ERR_UNSUPPORTED = -2, /* geometry outside what the kernels implement */
   QSA_ERR_WORKSPACE = -3,   /* workspace missing, too small or misaligned */
-  QSA_ERR_HIP = -4          /* a HIP launch or API call failed */
+  QSA_ERR_HIP = -4,         /* a HIP launch or API call failed */
+  QSA_ERR_TOO_LARGE = -5    /* the call needs more than the static scratch
+                               of qsa_decode_noalloc holds */
 } qsa_status;
 
 /* KV element formats of the paged cache (qsa-hisparse offload contract:
@@ -270,6 +273,37 @@ qsa_status qsa_prefill(const qsa_geometry* g, const qsa_paged_cache* cache,
                        const uint16_t* q, float* out, int32_t* out_groups,
                        int32_t* out_tokens, float* out_scores, void* ws,
                        size_t ws_bytes, void* stream);
+
+/* Size in bytes of the static device scratch that qsa_decode_noalloc uses
+ * in place of a workspace (one copy per GPU, held until the process ends). */
+#define QSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+size_t qsa_noalloc_scratch_bytes(void);
+
+/* qsa_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, semantics and
+ * results as qsa_decode; the workspace is instead a file-scope device
+ * array of QSA_NOALLOC_SCRATCH_BYTES (32 MiB) inside the library, one
+ * copy per GPU.  The call never allocates or frees device memory: the
+ * first call on a device only looks up that device's copy, with the
+ * device current.  It holds, e.g., 32 requests at 262,144 tokens with
+ * K = 2,048 groups (15.4 MiB; 8 such requests take 6.9 MiB).  A call whose
+ * workspace would exceed it (qsa_decode_workspace_size(...) >
+ * QSA_NOALLOC_SCRATCH_BYTES) returns QSA_ERR_TOO_LARGE after the argument
+ * checks of qsa_decode and before any HIP call.
+ *
+ * Every call on one GPU uses that GPU's single scratch area, which keeps
+ * whatever the last call left there (no call depends on it).  Calls that
+ * overlap on one GPU (on different streams, or from several threads
+ * without ordering) race on it and give undefined results: order them on
+ * one stream.  QSA_ERR_HIP is returned if the device's copy cannot be
+ * found. */
+qsa_status qsa_decode_noalloc(const qsa_geometry* g, const qsa_paged_cache* cache,
+                              int32_t batch, int32_t q_per_req, int32_t max_ctx,
+                              const int32_t* ctx_lens, const float* q_idx,
+                              const float* w_idx, const uint16_t* q, float* out,
+                              int32_t* out_groups, int32_t* out_tokens,
+                              float* out_scores, void* stream);
 
 /* Number of k̂ slots per request that qsa_append_kv reads from khat_new for
  * n_tokens new tokens: floor((n_tokens + 3) / 4), the most groups that

@@ -19,12 +19,13 @@ import os
 
 __all__ = ["QSAError", "load", "validate", "token_width", "index_topk_workspace_size",
            "decode_workspace_size", "prefill_workspace_size", "qsa_index_score",
-           "qsa_index_score_prefill", "qsa_index_topk", "qsa_decode", "qsa_prefill", "LIB_PATH"]
+           "qsa_index_score_prefill", "qsa_index_topk", "qsa_decode", "qsa_decode_noalloc",
+           "qsa_prefill", "noalloc_scratch_bytes", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsa.so")
 
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported geometry", -3: "workspace",
-          -4: "HIP error"}
+          -4: "HIP error", -5: "needs more than the static scratch of qsa_decode_noalloc"}
 
 
 class QSAError(RuntimeError):
@@ -83,6 +84,10 @@ def load():
         L.qsa_index_topk.argtypes = [G, C, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.qsa_decode.restype = ctypes.c_int
         L.qsa_decode.argtypes = [G, C, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.qsa_decode_noalloc.restype = ctypes.c_int
+        L.qsa_decode_noalloc.argtypes = [G, C, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.qsa_noalloc_scratch_bytes.restype = sz
+        L.qsa_noalloc_scratch_bytes.argtypes = []
         L.qsa_prefill.restype = ctypes.c_int
         L.qsa_prefill.argtypes = [G, C, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.qsa_append_khat_slots.restype = i32
@@ -247,6 +252,27 @@ def qsa_decode(geom, k_cache, v_cache, khat, page_table, ctx_lens, q_idx, w_idx,
                              *(_ptr(t) for t in args), _ptr(out), _ptr(groups), _ptr(tokens),
                              _ptr(scores), _ptr(ws), wsb, _stream(dev))
     _check("qsa_decode", code)
+    return dict(out=out, groups=groups, tokens=tokens, scores=scores)
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load().qsa_noalloc_scratch_bytes())
+
+
+def qsa_decode_noalloc(geom, k_cache, v_cache, khat, page_table, ctx_lens, q_idx, w_idx, q,
+                       max_ctx, q_per_req=1, out=None, groups=None, tokens=None, scores=None,
+                       num_pages=None):
+    """qsa_decode without a workspace: the library's static device scratch
+    stands in for it.  Every output is caller-supplied (None skips the
+    optional lists); the call itself allocates nothing on the device."""
+    g = _geom(geom)
+    c, keep = _cache(k_cache, v_cache, khat, page_table, num_pages)
+    args = [_c(ctx_lens), _c(q_idx), _c(w_idx), _c(q)]
+    code = load().qsa_decode_noalloc(ctypes.byref(g), ctypes.byref(c), int(ctx_lens.shape[0]),
+                                     int(q_per_req), int(max_ctx), *(_ptr(t) for t in args),
+                                     _ptr(out), _ptr(groups), _ptr(tokens), _ptr(scores),
+                                     _stream(q.device))
+    _check("qsa_decode_noalloc", code)
     return dict(out=out, groups=groups, tokens=tokens, scores=scores)
 
 

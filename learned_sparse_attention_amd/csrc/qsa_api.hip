@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "qsa.h"
 #include "qsa_device.h"
 #include "qsa_launch.h"
@@ -125,6 +127,31 @@ AttnArgs attn_args(const qsa_geometry* g, const qsa_paged_cache* c) {
     if ((call) != hipSuccess) return QSA_ERR_HIP;    \
   } while (0)
 
+// Scratch of qsa_decode_noalloc: a file-scope device array, one copy per
+// GPU, alive until the process ends.  Host code never passes the array's
+// name to a kernel or a copy (on the host it is only a stand-in for the
+// symbol): it uses the device address hipGetSymbolAddress returns for the
+// current device, looked up once per device.
+constexpr size_t kScratchBytes = (size_t)QSA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`, or null on failure.
+void* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -136,6 +163,8 @@ const char* qsa_status_string(qsa_status s) {
     case QSA_ERR_UNSUPPORTED: return "unsupported geometry";
     case QSA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case QSA_ERR_HIP: return "HIP error";
+    case QSA_ERR_TOO_LARGE:
+      return "call needs more scratch than the library's static scratch area holds";
   }
   return "unknown status";
 }
@@ -326,6 +355,34 @@ qsa_status qsa_prefill(const qsa_geometry* g, const qsa_paged_cache* cache, int3
     QSA_HIP(launch_expand_tokens(sel, g->topk_groups, n_q, 1, nullptr, first_pos, max_ctx,
                                  qsa_token_width(g, 1), out_tokens, s));
   return QSA_OK;
+}
+
+size_t qsa_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+qsa_status qsa_decode_noalloc(const qsa_geometry* g, const qsa_paged_cache* cache, int32_t batch,
+                              int32_t q_per_req, int32_t max_ctx, const int32_t* ctx_lens,
+                              const float* q_idx, const float* w_idx, const uint16_t* q,
+                              float* out, int32_t* out_groups, int32_t* out_tokens,
+                              float* out_scores, void* stream) {
+  // the argument checks of qsa_decode, then the size check, all before
+  // any HIP call
+  qsa_status st = qsa_validate(g);
+  if (st != QSA_OK) return st;
+  if (batch < 0 || q_per_req < 1 || q_per_req > 4 || max_ctx < 1 || max_ctx > kCapacity ||
+      !cache_ok(cache, true))
+    return QSA_ERR_INVALID_ARG;
+  if (q_per_req * (g->num_q_heads / g->num_kv_heads) > kMaxRows) return QSA_ERR_UNSUPPORTED;
+  if (max_ctx > cache->max_pages * kPage) return QSA_ERR_INVALID_ARG;
+  if (batch == 0) return QSA_OK;
+  if (!ctx_lens || !q_idx || !w_idx || !q || !out) return QSA_ERR_INVALID_ARG;
+  const size_t need = decode_layout(g, batch, q_per_req, max_ctx).total;
+  if (need > kScratchBytes) return QSA_ERR_TOO_LARGE;
+  void* ws = scratch_of_current_device();
+  if (!ws) return QSA_ERR_HIP;
+  // the decode kernels keep nothing in their workspace between calls, so
+  // the scratch needs no clearing
+  return qsa_decode(g, cache, batch, q_per_req, max_ctx, ctx_lens, q_idx, w_idx, q, out,
+                    out_groups, out_tokens, out_scores, ws, kScratchBytes, stream);
 }
 
 int32_t qsa_append_khat_slots(int32_t n_tokens) {
