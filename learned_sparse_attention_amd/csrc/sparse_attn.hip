@@ -73,8 +73,10 @@ struct SubTile {
 
 // One work item: the 16 query rows row_base .. row_base + 15 (row r =
 // position r / gq, head r % gq of the KV head's group; rows >= n_rows are
-// padding) over the item's token stream.
-template <bool kFp8>
+// padding) over the item's token stream.  kStreamV: V rows are read past
+// the caches (decode reads each selected row once); prefill keeps them
+// cacheable, since the queries of a chunk share the request's KV rows.
+template <bool kFp8, bool kStreamV>
 __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& it, int kvh,
                                             const uint16_t* q_rows, int q_row_stride,
                                             int row_base, int n_rows, int gq, float* acc_lds,
@@ -157,7 +159,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
 
   // K rows are fetched in four 16-byte pieces by separate instructions, so
   // they are cached normally (the pieces meet in L2); each lane's V piece is
-  // read once, whole, and streamed past the caches.
+  // read whole, once per item (streamed past the caches in decode).
   auto load = [&](SubTile<kFp8>& b, int s) {
     const int rk = tok_row[16 * s + lq];
     const uint8_t* kp = kc + ((size_t)max(rk, 0) * Hkv + kvh) * kRowBytes + 64 * lg * kEsize;
@@ -168,7 +170,9 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
       b.rv[j] = tok_row[16 * s + 4 * lg + j];
       const uint8_t* vp = vc + ((size_t)max(b.rv[j], 0) * Hkv + kvh) * kRowBytes + 16 * lq * kEsize;
 #pragma unroll
-      for (int i = 0; i < (kFp8 ? 1 : 2); ++i) b.v[j][i] = stream_load_u4(vp + 16 * i);
+      for (int i = 0; i < (kFp8 ? 1 : 2); ++i)
+        b.v[j][i] = kStreamV ? stream_load_u4(vp + 16 * i)
+                             : *reinterpret_cast<const u32x4*>(vp + 16 * i);
     }
   };
 
@@ -371,7 +375,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_decode_kernel(AttnArgs a
 
   const uint16_t* q_rows = a.q + ((size_t)b * Q * a.Hq + (size_t)kvh * gq) * kHeadDim;
   float* part = a.partial + (((size_t)b * a.Hkv + kvh) * a.n_splits + split) * n_rows * (2 + kHeadDim);
-  attend_item<kFp8>(a, it, kvh, q_rows, a.Hq * kHeadDim, rb * 16, n_rows, gq, acc_lds, ml_lds,
+  attend_item<kFp8, true>(a, it, kvh, q_rows, a.Hq * kHeadDim, rb * 16, n_rows, gq, acc_lds, ml_lds,
                     q_lds, tok_row, nullptr, part);
 }
 
@@ -397,7 +401,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs 
   it.base_len = L;
   const uint16_t* q_rows = a.q + ((size_t)qi * a.Hq + (size_t)kvh * gq) * kHeadDim;
   float* outp = a.out + ((size_t)qi * a.Hq + (size_t)kvh * gq) * kHeadDim;
-  attend_item<kFp8>(a, it, kvh, q_rows, 0, 0, gq, gq, acc_lds, ml_lds, q_lds, tok_row, outp,
+  attend_item<kFp8, false>(a, it, kvh, q_rows, 0, 0, gq, gq, acc_lds, ml_lds, q_lds, tok_row, outp,
                     nullptr);
 }
 
