@@ -61,15 +61,156 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Registers of one 16-token sub-tile in flight: lane l holds 64 contiguous
-// K bytes (fp8) / 128 bytes (bf16) of token lq = l % 16, and 16 / 32 bytes
-// of the V rows of tokens 4*lg + j (lg = l / 16).
+// Registers of one 16-token sub-tile in flight: lane l holds 64 (fp8) /
+// 128 (bf16) K bytes of token lq = l % 16, and 16 / 32 bytes of the V rows
+// of tokens 4*lg + j (lg = l / 16).
+//
+// Dimension order.  A dot product does not depend on the order of its terms,
+// so the contraction index of S^T = K . Q^T is permuted identically in both
+// operands, chosen so that the four lanes of one token read 64 contiguous
+// bytes of its K row in each load instruction (16 cache lines per
+// instruction rather than 64): in k-step ks, lane group lg supplies
+//   bf16 K: d = 32*ks + 8*lg + 0..7,
+//   fp8 K:  d = 64*(ks/2) + 16*lg + 8*(ks%2) + 0..7 (one 16-byte load
+//           serves two k-steps).
+// The output dimension of O^T = V^T . P^T is permuted through the V^T
+// operand: lane lq of m-block mb supplies d = dv(lq, mb) with
+//   bf16 V: dv = 8*lq + (mb % 8) + 128*(mb / 8) (two loads of 256
+//           contiguous bytes per token across the 16 lanes),
+//   fp8 V:  dv = 16*lq + mb (one load of the whole 256-byte row);
+// so accumulator acc[mb][i] of lane (lq, lg) holds output dimension
+// dv(4*lg + i, mb) of query row lq (out_dim below).
 template <bool kFp8>
 struct SubTile {
   u32x4 k[kFp8 ? 4 : 8];
   u32x4 v[4][kFp8 ? 1 : 2];
   int rv[4];  // physical rows of the four V tokens (-1: absent)
 };
+
+// First of the 8 dimensions that k-step ks of lane group lg covers.
+template <bool kFp8>
+__device__ __forceinline__ int qk_dim(int ks, int lg) {
+  return kFp8 ? 64 * (ks >> 1) + 16 * lg + 8 * (ks & 1) : 32 * ks + 8 * lg;
+}
+
+// Output dimension held in accumulator acc[mb][i] of lane group lg.
+template <bool kFp8>
+__device__ __forceinline__ int out_dim(int lg, int i, int mb) {
+  const int r = 4 * lg + i;
+  return kFp8 ? 16 * r + mb : 8 * r + (mb & 7) + 128 * (mb >> 3);
+}
+
+// Loads one 16-token sub-tile: K rows of the 16 tokens tok[0..16) (physical
+// row offsets, -1 if absent) and the V rows in MFMA operand order.  Each
+// lane's V pieces are read past the caches when kStreamV (decode reads each
+// selected row once).
+template <bool kFp8, bool kStreamV>
+__device__ __forceinline__ void load_subtile(SubTile<kFp8>& b, const int32_t* tok,
+                                             const uint8_t* kc, const uint8_t* vc, int Hkv,
+                                             int kvh) {
+  const int lane = threadIdx.x & (kWave - 1), lq = lane & 15, lg = lane >> 4;
+  constexpr int kEsize = kFp8 ? 1 : 2;
+  constexpr int kRowBytes = kHeadDim * kEsize;
+  const int rk = tok[lq];
+  // load i: bytes 64*i + 16*lg .. +15 of the K row (k-step i for bf16,
+  // k-steps 2i and 2i + 1 for fp8)
+  const uint8_t* kp = kc + ((size_t)max(rk, 0) * Hkv + kvh) * kRowBytes + 16 * lg;
+#pragma unroll
+  for (int i = 0; i < (kFp8 ? 4 : 8); ++i) b.k[i] = *reinterpret_cast<const u32x4*>(kp + 64 * i);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    b.rv[j] = tok[4 * lg + j];
+    // fp8: bytes 16*lq .. +15; bf16: elements 8*lq + 128*i .. +7 (i = 0, 1)
+    const uint8_t* vp = vc + ((size_t)max(b.rv[j], 0) * Hkv + kvh) * kRowBytes + 16 * lq;
+#pragma unroll
+    for (int i = 0; i < (kFp8 ? 1 : 2); ++i)
+      b.v[j][i] = kStreamV ? stream_load_u4(vp + 256 * i)
+                           : *reinterpret_cast<const u32x4*>(vp + 256 * i);
+  }
+}
+
+// One sub-tile's contribution to the online softmax of the 16 query rows:
+//   S^T = K . Q^T with Q^T operand qop[ks] (row lq, dims qk_dim(ks, lg) + 0..7);
+//   the weights of the visible tokens (vis[i] for D row 4*lg + i) update
+//   the running max m_run, sum l_run and O^T accumulators acc.
+template <bool kFp8>
+__device__ __forceinline__ void subtile_update(const SubTile<kFp8>& b, const u32x4 (&qop)[8],
+                                               const bool (&vis)[4], float qk_scale,
+                                               float& m_run, float& l_run, float4_t (&acc)[16]) {
+  float4_t sc = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    bf16x8 kop;
+    if (kFp8) {
+      const u32x4 w = b.k[ks / 2];
+      kop = (ks & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
+    } else {
+      kop = __builtin_bit_cast(bf16x8, b.k[ks]);
+    }
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, __builtin_bit_cast(bf16x8, qop[ks]), sc, 0,
+                                                0, 0);
+  }
+  float sv[4];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sv[i] = vis[i] ? sc[i] * qk_scale : -INFINITY;
+    tmax = fmaxf(tmax, sv[i]);
+  }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+  // Lazy running max: the accumulators are rescaled only when a row's max
+  // grows by more than 2^8, so weights stay <= 256.
+  const bool grow = tmax > m_run + 8.0f;
+  if (__any(grow)) {
+    const float m_new = grow ? tmax : m_run;
+    const float alpha = (m_run == -INFINITY || m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < 16; ++mb) acc[mb] *= alpha;
+    m_run = m_new;
+  }
+  // weights as a bf16 hi + lo pair (~16 significant bits) for the PV MFMA
+  float psum = 0.0f;
+  uint32_t hb[4], lb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float pw = (m_run == -INFINITY) ? 0.0f : exp2f(sv[i] - m_run);
+    hb[i] = bf16_rne_bits(pw);
+    lb[i] = bf16_rne_bits(pw - __uint_as_float(hb[i] << 16));
+    psum += pw;
+  }
+  l_run += psum;
+  const short4_t p_hi = (short4_t){(short)hb[0], (short)hb[1], (short)hb[2], (short)hb[3]};
+  const short4_t p_lo = (short4_t){(short)lb[0], (short)lb[1], (short)lb[2], (short)lb[3]};
+  // O^T += V^T . P^T; m-block mb holds d = out_dim(lg', i, mb) for D row 4*lg' + i
+#pragma unroll
+  for (int qd = 0; qd < 8; ++qd) {
+    uint32_t cv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (kFp8) {
+        const u32x4 w = b.rv[j] >= 0 ? b.v[j][0] : (u32x4){0u, 0u, 0u, 0u};
+        const uint32_t word = qd < 2 ? w.x : qd < 4 ? w.y : qd < 6 ? w.z : w.w;
+        cv[j] = (qd & 1) ? fp8x2_to_bf16x2<true>(word) : fp8x2_to_bf16x2<false>(word);
+      } else {
+        const u32x4 w = b.rv[j] >= 0 ? b.v[j][qd / 4] : (u32x4){0u, 0u, 0u, 0u};
+        const int e = qd % 4;
+        cv[j] = e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int mb = 2 * qd + h;
+      const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+      const uint32_t lo = __builtin_amdgcn_perm(cv[1], cv[0], sel);
+      const uint32_t hi = __builtin_amdgcn_perm(cv[3], cv[2], sel);
+      const short4_t vop = __builtin_bit_cast(short4_t, (u32x2){lo, hi});
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, p_hi, acc[mb], 0, 0, 0);
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, p_lo, acc[mb], 0, 0, 0);
+    }
+  }
+}
 
 // One work item: the 16 query rows row_base .. row_base + 15 (row r =
 // position r / gq, head r % gq of the KV head's group; rows >= n_rows are
@@ -85,8 +226,6 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int lq = lane & 15, lg = lane >> 4;
-  constexpr int kEsize = kFp8 ? 1 : 2;
-  constexpr int kRowBytes = kHeadDim * kEsize;
   constexpr int kQPitch = kHeadDim + 8;  // bf16 elements; spreads the 16 rows over LDS banks
 
   // ---- token stream -> physical row offsets (page * 64 + slot), -1 if absent
@@ -157,105 +296,25 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
   const uint8_t* vc = reinterpret_cast<const uint8_t*>(a.v);
   const int Hkv = a.Hkv;
 
-  // K rows are fetched in four 16-byte pieces by separate instructions, so
-  // they are cached normally (the pieces meet in L2); each lane's V piece is
-  // read whole, once per item (streamed past the caches in decode).
   auto load = [&](SubTile<kFp8>& b, int s) {
-    const int rk = tok_row[16 * s + lq];
-    const uint8_t* kp = kc + ((size_t)max(rk, 0) * Hkv + kvh) * kRowBytes + 64 * lg * kEsize;
-#pragma unroll
-    for (int i = 0; i < (kFp8 ? 4 : 8); ++i) b.k[i] = *reinterpret_cast<const u32x4*>(kp + 16 * i);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      b.rv[j] = tok_row[16 * s + 4 * lg + j];
-      const uint8_t* vp = vc + ((size_t)max(b.rv[j], 0) * Hkv + kvh) * kRowBytes + 16 * lq * kEsize;
-#pragma unroll
-      for (int i = 0; i < (kFp8 ? 1 : 2); ++i)
-        b.v[j][i] = kStreamV ? stream_load_u4(vp + 16 * i)
-                             : *reinterpret_cast<const u32x4*>(vp + 16 * i);
-    }
+    load_subtile<kFp8, kStreamV>(b, tok_row + 16 * s, kc, vc, Hkv, kvh);
   };
 
   auto compute = [&](const SubTile<kFp8>& b, int s) {
-    // S^T = K . Q^T (Q operand from LDS: row lq, d = 64*lg + 8*ks + 0..7)
-    float4_t sc = (float4_t){0.f, 0.f, 0.f, 0.f};
+    // Q operand from LDS: row lq, dims qk_dim(ks, lg) + 0..7
+    u32x4 qop[8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      bf16x8 kop;
-      if (kFp8) {
-        const u32x4 w = b.k[ks / 2];
-        kop = (ks & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
-      } else {
-        kop = __builtin_bit_cast(bf16x8, b.k[ks]);
-      }
-      const bf16x8 qop = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(q_lds + lq * kQPitch + 64 * lg + 8 * ks));
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop, sc, 0, 0, 0);
-    }
+    for (int ks = 0; ks < 8; ++ks)
+      qop[ks] = *reinterpret_cast<const u32x4*>(q_lds + lq * kQPitch + qk_dim<kFp8>(ks, lg));
     // token of D row 4*lg + i is stream entry 16s + 4*lg + i (= V token i)
-    float sv[4];
-    float tmax = -INFINITY;
+    bool vis[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int si = 16 * s + 4 * lg + i;
       const int tok = si < 4 * n_groups ? -1 : it.x_begin + (si - 4 * n_groups);  // -1: visible
-      const bool vis = b.rv[i] >= 0 && tok < limit;
-      sv[i] = vis ? sc[i] * qk_scale : -INFINITY;
-      tmax = fmaxf(tmax, sv[i]);
+      vis[i] = b.rv[i] >= 0 && tok < limit;
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    // Lazy running max: the accumulators (held in AGPRs) are rescaled only
-    // when a row's max grows by more than 2^8, so weights stay <= 256.
-    const bool grow = tmax > m_run + 8.0f;
-    if (__any(grow)) {
-      const float m_new = grow ? tmax : m_run;
-      const float alpha = (m_run == -INFINITY || m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < 16; ++mb) acc[mb] *= alpha;
-      m_run = m_new;
-    }
-    // weights as a bf16 hi + lo pair (~16 significant bits) for the PV MFMA
-    float psum = 0.0f;
-    uint32_t hb[4], lb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = (m_run == -INFINITY) ? 0.0f : exp2f(sv[i] - m_run);
-      hb[i] = bf16_rne_bits(p);
-      lb[i] = bf16_rne_bits(p - __uint_as_float(hb[i] << 16));
-      psum += p;
-    }
-    l_run += psum;
-    const short4_t p_hi = (short4_t){(short)hb[0], (short)hb[1], (short)hb[2], (short)hb[3]};
-    const short4_t p_lo = (short4_t){(short)lb[0], (short)lb[1], (short)lb[2], (short)lb[3]};
-    // O^T += V^T . P^T; m-block mb holds d = 64*lg' + 16*i + mb for D row 4*lg' + i
-#pragma unroll
-    for (int qd = 0; qd < 8; ++qd) {
-      uint32_t cv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (kFp8) {
-          const u32x4 w = b.rv[j] >= 0 ? b.v[j][0] : (u32x4){0u, 0u, 0u, 0u};
-          const uint32_t word = qd < 2 ? w.x : qd < 4 ? w.y : qd < 6 ? w.z : w.w;
-          cv[j] = (qd & 1) ? fp8x2_to_bf16x2<true>(word) : fp8x2_to_bf16x2<false>(word);
-        } else {
-          const u32x4 w = b.rv[j] >= 0 ? b.v[j][qd / 4] : (u32x4){0u, 0u, 0u, 0u};
-          const int e = qd % 4;
-          cv[j] = e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int mb = 2 * qd + h;
-        const uint32_t sel = h ? 0x07060302u : 0x05040100u;
-        const uint32_t lo = __builtin_amdgcn_perm(cv[1], cv[0], sel);
-        const uint32_t hi = __builtin_amdgcn_perm(cv[3], cv[2], sel);
-        const short4_t vop = __builtin_bit_cast(short4_t, (u32x2){lo, hi});
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, p_hi, acc[mb], 0, 0, 0);
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, p_lo, acc[mb], 0, 0, 0);
-      }
-    }
+    subtile_update<kFp8>(b, qop, vis, qk_scale, m_run, l_run, acc);
   };
 
   // ---- main loop: rounds of kNS sub-tiles per wave (sub-tiles
@@ -296,7 +355,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
 #pragma unroll
       for (int mb = 0; mb < 16; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rowp[64 * lg + 16 * i + mb] = acc[mb][i] * fac;
+        for (int i = 0; i < 4; ++i) rowp[out_dim<kFp8>(lg, i, mb)] = acc[mb][i] * fac;
     }
   }
   // row statistics: common max and the sum of the rescaled row sums
@@ -405,28 +464,275 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs 
                     nullptr);
 }
 
+// ---------------------------------------------------------------------------
+// Prefill attention over token partitions.
+//
+// The queries of a chunk gather their selected rows from the whole request
+// cache (64 MiB for 32,768 BF16 tokens and two KV heads), far more than one
+// XCD's 4 MiB L2, so a kernel that gives each workgroup one query's whole
+// selection reads most rows from beyond L2.  Here the token axis is cut into
+// ranges of R tokens whose K and V rows for one KV head take about 2 MiB; a
+// partition is (range, KV head).  Workgroups are numbered so that each XCD
+// works through its partitions one after another, each for every query of
+// the chunk, so the current partition's rows stay in that XCD's L2.  A
+// workgroup takes one partition and four consecutive queries, one per
+// wavefront; a wavefront attends over its query's selected tokens inside
+// the range and writes (max, sum, accumulator) rows for the query's heads
+// of that KV head, which combine_kernel merges over the ranges.
+
+constexpr int kXcds = 8;
+constexpr int kRangePitch = kHeadDim + 4;  // partial row: max, sum, 2 unused, accumulator
+// Bytes of K and V rows of one KV head per range (an XCD's L2 holds 4 MiB;
+// measured on the 4,096-query chunk over 32,768 BF16 tokens: 2 MiB ranges
+// 1,824 us per prefill step, 4 MiB 1,648 us, 8 MiB 1,608 us, the per-query
+// kernel 1,950 us).
+#ifndef QSA_RANGE_KIB
+#define QSA_RANGE_KIB 8192
+#endif
+constexpr int kRangeBytes = QSA_RANGE_KIB << 10;
+// 16-token sub-tiles each wavefront keeps in flight (bf16 K/V; fp8 takes 2).
+#ifndef QSA_BF16_SUBTILES
+#define QSA_BF16_SUBTILES 1
+#endif
+constexpr int kRangeTok = 1024;            // stream entries translated at a time per wavefront
+constexpr int kRangeGpl = kRangeTok / (kRatio * kWave);  // groups per lane per translation step
+
+// Floats of LDS per wavefront: the token rows of one translation step, then
+// (reused) the transposed partial rows of the query's gq heads.
+__host__ __device__ constexpr int range_wave_floats(int gq) {
+  return gq * kRangePitch > kRangeTok + 16 ? gq * kRangePitch : kRangeTok + 16;
+}
+
+// off[q * (NR + 1) + r] = number of entries of query q's selection (ascending
+// group ids, -1 padded) whose group lies below range r (group < r * R / 4),
+// r = 0 .. NR.  One wavefront per query; lane l holds a run of consecutive
+// entries.  Since the entries ascend, off[r] is the index of the first
+// entry at or past range r: each entry e writes the boundaries between the
+// range of entry e - 1 and its own, so every boundary is written once.
+__global__ __launch_bounds__(kAttnThreads) void range_offsets_kernel(
+    const int32_t* __restrict__ sel, int K, int n_q, int R, int NR, int32_t* __restrict__ off) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int q = blockIdx.x * kAttnWaves + w;
+  if (q >= n_q) return;
+  constexpr int kPer = 2048 / kWave;  // entries per lane at the largest budget
+  const int per = (K + kWave - 1) / kWave;
+  const int gpr = R / kRatio;  // groups per range
+  const int32_t* row = sel + (size_t)q * K;
+  int32_t* o = off + (size_t)q * (NR + 1);
+  int v[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = lane * per + i;
+    v[i] = (i < per && e < K) ? row[e] : -1;
+  }
+  // the largest entry of this lane's run (the valid entries are a prefix of
+  // the row, ascending), and the number of valid entries
+  int last = -1, n_valid = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    last = max(last, v[i]);
+    n_valid += v[i] >= 0 ? 1 : 0;
+  }
+#pragma unroll
+  for (int o2 = 32; o2 >= 1; o2 >>= 1) n_valid += __shfl_xor(n_valid, o2, kWave);
+  int prev = __shfl_up(last, 1, kWave);
+  if (lane == 0) prev = -1;
+  int prev_r = prev >= 0 ? prev / gpr : -1;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (v[i] >= 0) {
+      const int e = lane * per + i;
+      const int rr = min(v[i] / gpr, NR);
+      for (int b = prev_r + 1; b <= rr; ++b) o[b] = e;
+      prev_r = max(prev_r, rr);
+    }
+  }
+  // boundaries past the last valid entry's range (all of them when the
+  // selection is empty)
+  const int last_g = n_valid > 0 ? row[n_valid - 1] : -1;
+  const int last_r = last_g >= 0 ? min(last_g / gpr, NR) : -1;
+  for (int b = last_r + 1 + lane; b <= NR; b += kWave) o[b] = n_valid;
+}
+
+template <bool kFp8>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_ranges_kernel(
+    AttnArgs a, int R, int NR, int n_qb, const int32_t* __restrict__ off,
+    float* __restrict__ part) {
+  extern __shared__ float smem[];
+  const int gq = a.Hq / a.Hkv;
+  // workgroup -> (partition p, query block qb): XCD x (= blockIdx % 8, the
+  // order in which workgroups are dealt to the XCDs) takes partitions
+  // x, x + 8, ... in turn, every query block of one before the next
+  const int b = blockIdx.x;
+  const int xcd = b % kXcds, i = b / kXcds;
+  const int j = i / n_qb, qb = i - j * n_qb;
+  const int p = kXcds * j + xcd;
+  if (p >= NR * a.Hkv) return;  // padding partition: the whole workgroup leaves
+  const int r = p / a.Hkv, kvh = p - r * a.Hkv;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int lq = lane & 15, lg = lane >> 4;
+  const int q = qb * kAttnWaves + wave;
+  if (q >= a.batch) return;  // whole wavefronts; nothing below synchronises the block
+  float* wl = smem + (size_t)wave * range_wave_floats(gq);
+  int32_t* tok = reinterpret_cast<int32_t*>(wl);
+
+  // the query's selected groups and current-block tokens inside the range
+  const int L = a.first_pos + q + 1;
+  const int G = L / kRatio;
+  const int n_valid = min(a.K, G);
+  const int t0 = r * R, t1 = min(t0 + R, L);
+  int lo = 0, hi = 0, x0 = 0, x1 = 0;
+  if (t0 < L) {
+    lo = min(off[(size_t)q * (NR + 1) + r], n_valid);
+    hi = min(off[(size_t)q * (NR + 1) + r + 1], n_valid);
+    x0 = max(kRatio * G, t0);
+    x1 = max(x0, t1);
+  }
+  const int n_groups = max(0, hi - lo), n_extra = x1 - x0;
+  const int n_stream = kRatio * n_groups + n_extra;
+
+  // the query rows as the Q^T operand, held in registers: row lq (head
+  // kvh * gq + lq, zero past gq), dims qk_dim(ks, lg) + 0..7
+  u32x4 qop[8];
+  {
+    const uint16_t* qr = a.q + ((size_t)q * a.Hq + (size_t)kvh * gq + min(lq, gq - 1)) * kHeadDim;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qr + qk_dim<kFp8>(ks, lg));
+      qop[ks] = lq < gq ? v : (u32x4){0u, 0u, 0u, 0u};
+    }
+  }
+  const float qk_scale = a.sm_scale * a.k_scale * kLog2e;
+  float m_run = -INFINITY, l_run = 0.0f;
+  float4_t acc[16];
+#pragma unroll
+  for (int mb = 0; mb < 16; ++mb) acc[mb] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  const uint8_t* kc = reinterpret_cast<const uint8_t*>(a.k);
+  const uint8_t* vc = reinterpret_cast<const uint8_t*>(a.v);
+  const int32_t* pt = a.page_table + (size_t)a.req * a.max_pages;
+  const int32_t* srow = a.sel + (size_t)q * a.K + lo;
+
+  constexpr int kNS = kFp8 ? 2 : QSA_BF16_SUBTILES;  // sub-tiles in flight per wavefront
+  for (int c0 = 0; c0 < n_stream; c0 += kRangeTok) {
+    // stream entries c0 + 4*(u*64 + lane) .. + 3 -> physical rows: a selected
+    // group's four tokens (one page), or up to four current-block tokens.
+    // All of a lane's selection loads are issued before its page-table
+    // loads, so a step costs two memory round trips.
+    {
+      int gs[kRangeGpl], ph[kRangeGpl];
+#pragma unroll
+      for (int u = 0; u < kRangeGpl; ++u) {
+        const int e = c0 + kRatio * (u * kWave + lane);
+        gs[u] = e < kRatio * n_groups ? srow[e / kRatio] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kRangeGpl; ++u) ph[u] = gs[u] >= 0 ? pt[(kRatio * gs[u]) / kPage] : -1;
+#pragma unroll
+      for (int u = 0; u < kRangeGpl; ++u) {
+        const int e = c0 + kRatio * (u * kWave + lane);
+        int4 rr = make_int4(-1, -1, -1, -1);
+        if (e < kRatio * n_groups) {
+          if (gs[u] >= 0 && ph[u] >= 0 && ph[u] < a.num_pages) {
+            const int base = ph[u] * kPage + (kRatio * gs[u]) % kPage;
+            rr = make_int4(base, base + 1, base + 2, base + 3);
+          }
+        } else if (e < n_stream) {
+          int t4[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int sx = e + k - kRatio * n_groups;
+            t4[k] = -1;
+            if (sx >= 0 && sx < n_extra) {
+              const int t = x0 + sx;
+              const int pg = pt[t / kPage];
+              if (pg >= 0 && pg < a.num_pages) t4[k] = pg * kPage + t % kPage;
+            }
+          }
+          rr = make_int4(t4[0], t4[1], t4[2], t4[3]);
+        }
+        *reinterpret_cast<int4*>(tok + kRatio * (u * kWave + lane)) = rr;
+      }
+    }
+    // LDS operations of one wavefront execute in order; the fences keep the
+    // compiler from moving the reads below above the writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int n_sub = min(kRangeTok / 16, (n_stream - c0 + 15) / 16);
+    for (int s = 0; s < n_sub; s += kNS) {
+      SubTile<kFp8> bt[kNS];
+#pragma unroll
+      for (int u = 0; u < kNS; ++u)
+        if (s + u < n_sub)
+          load_subtile<kFp8, false>(bt[u], tok + 16 * (s + u), kc, vc, a.Hkv, kvh);
+#pragma unroll
+      for (int u = 0; u < kNS; ++u) {
+        if (s + u < n_sub) {
+          bool vis[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) vis[k] = bt[u].rv[k] >= 0;
+          subtile_update<kFp8>(bt[u], qop, vis, qk_scale, m_run, l_run, acc);
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // ---- the partial rows: row lq's sum over its four lanes, then the
+  // accumulator transposed through LDS (acc[mb][i] of lane (lq, lg) is
+  // dimension out_dim(lg, i, mb); runs of four consecutive mb are four
+  // consecutive dimensions) and written with 16-byte stores
+  float l = l_run;
+  l += __shfl_xor(l, 16, kWave);
+  l += __shfl_xor(l, 32, kWave);
+  if (lq < gq) {
+    float* rowp = wl + lq * kRangePitch;
+    if (lg == 0) *reinterpret_cast<float4*>(rowp) = make_float4(m_run, l, 0.0f, 0.0f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<float4*>(rowp + 4 + out_dim<kFp8>(lg, i, 4 * c)) =
+            make_float4(acc[4 * c][i], acc[4 * c + 1][i], acc[4 * c + 2][i], acc[4 * c + 3][i]);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float4* dst = reinterpret_cast<float4*>(part + (((size_t)q * a.Hkv + kvh) * NR + r) * gq *
+                                                     kRangePitch);
+  const float4* srcl = reinterpret_cast<const float4*>(wl);
+  const int nf4 = gq * (kRangePitch / 4);
+  for (int e = lane; e < nf4; e += kWave) dst[e] = srcl[e];
+}
+
 // Merge split partials: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
 // Thread s first fetches split s's (m, l) so all splits are read at once;
 // then thread d sums the accumulators with independent loads.
+// A partial row is `pitch` floats: max, sum, then the accumulator from
+// float `acc_off` on (decode: pitch 2 + 256, offset 2; prefill ranges:
+// 16-byte aligned rows of 260, offset 4).
 constexpr int kMaxSplits = kHeadDim;
 __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restrict__ partial,
                                                            int n_splits, int Hq, int Hkv, int Q,
-                                                           float v_scale, float* __restrict__ out) {
+                                                           float v_scale, float* __restrict__ out,
+                                                           int pitch, int acc_off) {
   __shared__ float fac[kMaxSplits];
   __shared__ float red[kHeadDim / kWave];
   const int h = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int gq = Hq / Hkv, kvh = h / gq, r = j * gq + (h % gq);
   const int R = Q * gq;
-  const size_t split_stride = (size_t)R * (2 + kHeadDim);
+  const size_t split_stride = (size_t)R * pitch;
   const float* p = partial + ((size_t)(b * Hkv + kvh) * n_splits) * split_stride +
-                   (size_t)r * (2 + kHeadDim);
+                   (size_t)r * pitch;
   const int t = threadIdx.x, lane = t & (kWave - 1), wid = t / kWave;
   // the first kEarly splits' accumulators are fetched together with the
   // (max, sum) pairs, so both come back in one memory round trip
   constexpr int kEarly = 32;
   float early[kEarly];
 #pragma unroll
-  for (int s = 0; s < kEarly; ++s) early[s] = s < n_splits ? p[s * split_stride + 2 + t] : 0.0f;
+  for (int s = 0; s < kEarly; ++s) early[s] = s < n_splits ? p[s * split_stride + acc_off + t] : 0.0f;
   const float m = t < n_splits ? p[t * split_stride] : -INFINITY;
   const float l = t < n_splits ? p[t * split_stride + 1] : 0.0f;
   float M = wave_max(m);
@@ -444,7 +750,7 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restri
 #pragma unroll
   for (int s = 0; s < kEarly; ++s) num += fac[s] * early[s];  // fac[s] = 0 past n_splits
 #pragma unroll 8
-  for (int s = kEarly; s < n_splits; ++s) num += fac[s] * p[s * split_stride + 2 + t];
+  for (int s = kEarly; s < n_splits; ++s) num += fac[s] * p[s * split_stride + acc_off + t];
   out[(((size_t)b * Q + j) * Hq + h) * kHeadDim + t] = den > 0.0f ? num * (v_scale / den) : 0.0f;
 }
 
@@ -488,16 +794,44 @@ hipError_t launch_decode_t(const AttnArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   dim3 cgrid(a.Hq, a.q_per_req, a.batch);
   hipLaunchKernelGGL(combine_kernel, cgrid, dim3(kHeadDim), 0, stream, a.partial, a.n_splits, a.Hq,
-                     a.Hkv, a.q_per_req, a.v_scale, a.out);
+                     a.Hkv, a.q_per_req, a.v_scale, a.out, 2 + kHeadDim, 2);
   return hipGetLastError();
 }
 
-template <bool kFp8>
-hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
+// FP8 K/V: one workgroup per (query, KV head) over the query's whole
+// selection.  Its rows are half the size of BF16 rows, and the per-query
+// kernel already finds over half of them in L2 (measured: 1,010 us per
+// prefill step of the 4,096-query chunk against 1,143 us with ranges).
+hipError_t launch_prefill_per_query(const AttnArgs& a, hipStream_t stream) {
   if (a.Hq / a.Hkv > 16) return hipErrorInvalidValue;
   const size_t smem = attn_smem_bytes(4 * a.K + 3);
   dim3 grid(a.batch, a.Hkv);
-  hipLaunchKernelGGL((attn_prefill_kernel<kFp8>), grid, dim3(kAttnThreads), smem, stream, a);
+  hipLaunchKernelGGL((attn_prefill_kernel<true>), grid, dim3(kAttnThreads), smem, stream, a);
+  return hipGetLastError();
+}
+
+// BF16 K/V: range partitions (attn_prefill_ranges_kernel), then the merge.
+template <bool kFp8>
+hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
+  if (a.Hq / a.Hkv > 16) return hipErrorInvalidValue;
+  if (!a.range_offsets || !a.partial) return hipErrorInvalidValue;
+  int R, NR;
+  prefill_ranges(a.kv_dtype, a.Hkv, a.max_ctx, &R, &NR);
+  const int n_qb = (a.batch + kAttnWaves - 1) / kAttnWaves;
+  hipLaunchKernelGGL(range_offsets_kernel, dim3(n_qb), dim3(kAttnThreads), 0, stream, a.sel, a.K,
+                     a.batch, R, NR, a.range_offsets);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int gq = a.Hq / a.Hkv;
+  const int np_pad = (NR * a.Hkv + kXcds - 1) / kXcds * kXcds;
+  const size_t smem = sizeof(float) * (size_t)kAttnWaves * range_wave_floats(gq);
+  hipLaunchKernelGGL((attn_prefill_ranges_kernel<kFp8>), dim3((unsigned)((size_t)n_qb * np_pad)),
+                     dim3(kAttnThreads), smem, stream, a, R, NR, n_qb, a.range_offsets, a.partial);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 cgrid(a.Hq, 1, a.batch);
+  hipLaunchKernelGGL(combine_kernel, cgrid, dim3(kHeadDim), 0, stream, a.partial, NR, a.Hq, a.Hkv,
+                     1, a.v_scale, a.out, kRangePitch, 4);
   return hipGetLastError();
 }
 
@@ -506,11 +840,39 @@ hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
 // then mostly come from the caches.
 hipError_t dispatch(const AttnArgs& a, hipStream_t stream, bool prefill) {
   if (a.kv_dtype == 1)
-    return prefill ? launch_prefill_t<true>(a, stream) : launch_decode_t<true>(a, stream);
+    return prefill ? launch_prefill_per_query(a, stream) : launch_decode_t<true>(a, stream);
   return prefill ? launch_prefill_t<false>(a, stream) : launch_decode_t<false>(a, stream);
 }
 
 }  // namespace
+
+void prefill_ranges(int kv_dtype, int Hkv, int max_ctx, int* R, int* NR) {
+  // K + V rows of one KV head for R tokens take kRangeBytes; at least 8
+  // partitions so every XCD has one; at most 32 ranges
+  const int esize = kv_dtype == 1 ? 1 : 2;
+  const int r_l2 = kRangeBytes / (2 * kHeadDim * esize);
+  const int ctx = max(max_ctx, 1);
+  int nr = (ctx + r_l2 - 1) / r_l2;
+  nr = max(nr, (kXcds + Hkv - 1) / Hkv);
+  nr = min(nr, 32);
+  int r = (ctx + nr - 1) / nr;
+  r = (r + kPage - 1) / kPage * kPage;
+  *R = r;
+  *NR = (ctx + r - 1) / r;
+}
+
+size_t prefill_attn_workspace_bytes(int kv_dtype, int Hq, int Hkv, int n_q, int max_ctx,
+                                    size_t* off_bytes) {
+  if (kv_dtype == 1) {  // the per-query kernel needs no workspace
+    if (off_bytes) *off_bytes = 0;
+    return 0;
+  }
+  int R, NR;
+  prefill_ranges(kv_dtype, Hkv, max_ctx, &R, &NR);
+  const size_t ob = ((size_t)n_q * (NR + 1) * sizeof(int32_t) + 255) / 256 * 256;
+  if (off_bytes) *off_bytes = ob;
+  return ob + sizeof(float) * (size_t)n_q * Hkv * NR * (Hq / Hkv) * kRangePitch;
+}
 
 hipError_t launch_sparse_attn_decode(const AttnArgs& a, hipStream_t stream) {
   if (a.batch <= 0) return hipSuccess;
