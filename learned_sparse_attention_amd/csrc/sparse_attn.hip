@@ -134,9 +134,20 @@ __device__ __forceinline__ void load_subtile(SubTile<kFp8>& b, const int32_t* to
 //   the weights of the visible tokens (vis[i] for D row 4*lg + i) update
 //   the running max m_run, sum l_run and O^T accumulators acc.
 template <bool kFp8>
-__device__ __forceinline__ void subtile_update(const SubTile<kFp8>& b, const u32x4 (&qop)[8],
+__device__ __forceinline__ void subtile_update(SubTile<kFp8>& b, const u32x4 (&qop)[8],
                                                const bool (&vis)[4], float qk_scale,
                                                float& m_run, float& l_run, float4_t (&acc)[16]) {
+  // Absent tokens (padding, out-of-range pages) were loaded from row 0 of
+  // the cache, which may hold anything: their V operands are cleared so a
+  // zero weight cannot meet a NaN.  Nearly every sub-tile is full, so the
+  // clearing runs only when the wavefront holds an absent token.
+  if (!__all(b.rv[0] >= 0 && b.rv[1] >= 0 && b.rv[2] >= 0 && b.rv[3] >= 0)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < (kFp8 ? 1 : 2); ++i)
+        if (b.rv[j] < 0) b.v[j][i] = (u32x4){0u, 0u, 0u, 0u};
+  }
   float4_t sc = (float4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
@@ -190,11 +201,11 @@ __device__ __forceinline__ void subtile_update(const SubTile<kFp8>& b, const u32
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (kFp8) {
-        const u32x4 w = b.rv[j] >= 0 ? b.v[j][0] : (u32x4){0u, 0u, 0u, 0u};
+        const u32x4 w = b.v[j][0];
         const uint32_t word = qd < 2 ? w.x : qd < 4 ? w.y : qd < 6 ? w.z : w.w;
         cv[j] = (qd & 1) ? fp8x2_to_bf16x2<true>(word) : fp8x2_to_bf16x2<false>(word);
       } else {
-        const u32x4 w = b.rv[j] >= 0 ? b.v[j][qd / 4] : (u32x4){0u, 0u, 0u, 0u};
+        const u32x4 w = b.v[j][qd / 4];
         const int e = qd % 4;
         cv[j] = e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
       }
@@ -300,7 +311,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
     load_subtile<kFp8, kStreamV>(b, tok_row + 16 * s, kc, vc, Hkv, kvh);
   };
 
-  auto compute = [&](const SubTile<kFp8>& b, int s) {
+  auto compute = [&](SubTile<kFp8>& b, int s) {
     // Q operand from LDS: row lq, dims qk_dim(ks, lg) + 0..7
     u32x4 qop[8];
 #pragma unroll
