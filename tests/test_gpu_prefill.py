@@ -221,3 +221,35 @@ def test_prefill_head_shapes(gpu, hq, hkv, n_q, kv):
 def test_prefill_topk_paths_and_budgets(gpu, first_pos, n_q, K, kv):
     wl = workload.prefill_workload(840 + K, first_pos, n_q, kv_dtype=kv, topk_groups=K)
     _prefill_check(wl, gpu, _sample_rows(wl.n_q, 6))
+
+
+# BF16 prefill attention works on token-range partitions (ranges whose K
+# and V rows for one KV head take 8 MiB, at most 32 ranges); the cases
+# below stress the per-range bookkeeping: few selected groups per range,
+# the 32-range cap at full capacity, and selections piled into one range.
+
+@pytest.mark.parametrize("K", [1, 7, 100])
+def test_prefill_ranges_small_budgets(gpu, K):
+    wl = workload.prefill_workload(860 + K, 20000, 300, kv_dtype="bf16", topk_groups=K)
+    _prefill_check(wl, gpu, np.arange(wl.n_q))
+
+
+def test_prefill_ranges_at_full_capacity(gpu):
+    # 64 queries ending a 262,144-token request: 32 ranges of 8,192 tokens
+    wl = workload.prefill_workload(863, 262144 - 64, 64, kv_dtype="bf16", topk_groups=2048)
+    assert wl.first_pos + wl.n_q == 262144
+    _prefill_check(wl, gpu, np.arange(wl.n_q))
+
+
+def test_prefill_ranges_selection_in_one_range(gpu):
+    # every query shares one indexer query, and the groups of tokens
+    # 16,384 .. 24,575 (one 8,192-token range) score far above the rest:
+    # each selection lies wholly in that range, the others hold only the
+    # current block
+    wl = workload.prefill_workload(864, 30000, 96, kv_dtype="bf16", topk_groups=512)
+    wl.q_idx[:] = wl.q_idx[0]
+    wl.w_idx[:] = wl.w_idx[0]
+    for g in range(16384 // 4, 24576 // 4):
+        wl.khat[wl.page_table[0, g // 16], g % 16] = 4.0 * wl.q_idx[0]
+    _, gg = _prefill_check(wl, gpu, np.arange(wl.n_q))
+    assert np.all((gg >= 16384 // 4) & (gg < 24576 // 4))
