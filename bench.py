@@ -249,6 +249,48 @@ def write_mfma_counters(pmc_dir: str, commands: list, out_dir: str = None) -> No
     print(json.dumps(rec))
 
 
+def write_trace(trace_dir: str, commands: list, out_dir: str = None) -> str:
+    """Turn a rocprofv3 --kernel-trace --stats run of this script into the
+    kernel-time table of profiles/qsa_decode__<workload>.kernel_trace.md
+    (durations in microseconds, per kernel: calls, mean, min, max, share)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows = []
+    for fn in files:
+        with open(fn, newline="") as f:
+            rows += list(csv.DictReader(f))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["# Kernel trace: bench.py (decode B8 at 262,144 tokens, FP8 E4M3 KV, K = 2,048 groups; "
+             "prefill chunk of 4,096 queries; cache append; multi-query indexer legs)", "",
+             "Command (from the repository root, on one MI355X):", "",
+             *[f"    {c}" for c in commands], "",
+             "rocprofv3 kernel statistics (durations in microseconds).  bench.py times the decode "
+             "step (one `qsa_decode`: index_score_gemv_kernel, topk_extract_kernel, "
+             "topk_finish_kernel, attn_decode_kernel, combine_kernel), the indexer GEMV alone, "
+             "the prefill scoring alone and whole `qsa_prefill` steps on the 4,096-query chunk "
+             "(BF16: index_score_mfma_kernel, topk_row_kernel, range_offsets_kernel, "
+             "attn_prefill_ranges_kernel, combine_ranges_kernel; FP8: attn_prefill_kernel in place of "
+             "the range kernels), the cache append, and the multi-query indexer legs "
+             "(`Form<4, 1, 128>` is the shared-key form, `Form<8, 8, 64>` the per-head form).", "",
+             "| kernel | calls | average | min | max | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("qsa::(anonymous namespace)::", "").replace("void ", "")
+        name = name.split("(")[0]
+        lines.append(f"| {name[:110]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{100 * float(r['TotalDurationNs']) / total:.1f}% |")
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    path = os.path.join(out_dir, f"qsa_decode__{WORKLOAD_SLUG[3]}.kernel_trace.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
 def measured_mfma_util(form: str, profiles_dir: str = None):
     """Matrix-core utilisation of index_score_mfma_kernel<form> from the
     committed counter summary, if it was taken on the current kernel source;
@@ -313,6 +355,29 @@ def prefill_scoring(dev, steps: int, warmup: int) -> dict:
     e1.record()
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / n_step
+    del d, sc, out, ws
+    # the same chunk with FP8 E4M3 K/V (its attention takes the per-query kernel)
+    wf = workload.prefill_workload(workload.CONFIG_SEED + 4, 28672, 4096, kv_dtype="fp8",
+                                   topk_groups=512)
+    df = workload.to_device(wf, dev)
+    outf = torch.empty((wf.n_q, 16, 256), dtype=torch.float32, device=dev)
+    wsf = torch.empty(qsa.prefill_workspace_size(wf.geom, wf.n_q, wf.first_pos + wf.n_q),
+                      dtype=torch.uint8, device=dev)
+
+    def step_fp8():
+        qsa.qsa_prefill(wf.geom, df["k"], df["v"], df["khat"], df["pt"], wf.req, wf.first_pos,
+                        df["q_idx"], df["w_idx"], df["q"], out=outf, workspace=wsf,
+                        num_pages=wf.num_pages)
+
+    step_fp8()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n_step):
+        step_fp8()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step_fp8 = e0.elapsed_time(e1) / n_step
+    del df, outf, wsf
     tflops = visible / (ms * 1e-3) / 1e12
     return {"workload": "prefill chunk of 4,096 queries at positions 28,672..32,767, "
                         "8,192 groups, 8 heads x 64, BF16 KV, K=512 groups",
@@ -322,7 +387,7 @@ def prefill_scoring(dev, steps: int, warmup: int) -> dict:
             "flops_per_launch": visible, "dense_tile_flops": dense, "ms_per_launch": ms,
             "score_bytes_written": wl.n_q * gstride * 4,
             "mfma_util_counters": measured_mfma_util("Form<8, 8, 64>"),
-            "prefill_step_ms": ms_step}
+            "prefill_step_ms": ms_step, "prefill_step_fp8_ms": ms_step_fp8}
 
 
 def mqa_indexer(dev, steps: int, warmup: int) -> dict:
@@ -501,9 +566,14 @@ def main() -> int:
     ap.add_argument("--write-mfma-counters", metavar="PMC_DIR",
                     help="no GPU: summarise a rocprofv3 --pmc run of the matrix-core counters "
                          "into profiles/")
+    ap.add_argument("--write-trace", metavar="TRACE_DIR",
+                    help="no GPU: summarise a rocprofv3 --kernel-trace --stats run into profiles/")
     ap.add_argument("--counter-commands", nargs="*", default=[],
                     help="the commands that made the counter runs (recorded with them)")
     args = ap.parse_args()
+    if args.write_trace:
+        print(write_trace(args.write_trace, args.counter_commands))
+        return 0
     if args.write_mfma_counters:
         write_mfma_counters(args.write_mfma_counters, args.counter_commands)
         return 0

@@ -28,7 +28,8 @@
 // makes those contiguous loads possible.  Waves merge their (max, sum,
 // accumulator) through LDS at the end.  Decode splits the selection over
 // several workgroups and writes (max, sum, accumulator) partials that
-// combine_kernel merges; prefill writes normalised rows directly.
+// combine_kernel merges.  Prefill over FP8 caches writes normalised rows
+// directly; over BF16 caches it works in token-range partitions (below).
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
@@ -489,7 +490,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs 
 // workgroup takes one partition and four consecutive queries, one per
 // wavefront; a wavefront attends over its query's selected tokens inside
 // the range and writes (max, sum, accumulator) rows for the query's heads
-// of that KV head, which combine_kernel merges over the ranges.
+// of that KV head, which combine_ranges_kernel merges over the ranges.
 
 constexpr int kXcds = 8;
 constexpr int kRangePitch = kHeadDim + 4;  // partial row: max, sum, 2 unused, accumulator
@@ -516,53 +517,62 @@ __host__ __device__ constexpr int range_wave_floats(int gq) {
 
 // off[q * (NR + 1) + r] = number of entries of query q's selection (ascending
 // group ids, -1 padded) whose group lies below range r (group < r * R / 4),
-// r = 0 .. NR.  One wavefront per query; lane l holds a run of consecutive
-// entries.  Since the entries ascend, off[r] is the index of the first
-// entry at or past range r: each entry e writes the boundaries between the
+// r = 0 .. NR.  One wavefront per query reads the row in coalesced chunks
+// of 64 entries.  Since the entries ascend, off[r] is the index of the
+// first entry at or past range r: entry e writes the boundaries between the
 // range of entry e - 1 and its own, so every boundary is written once.
 __global__ __launch_bounds__(kAttnThreads) void range_offsets_kernel(
     const int32_t* __restrict__ sel, int K, int n_q, int R, int NR, int32_t* __restrict__ off) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int q = blockIdx.x * kAttnWaves + w;
   if (q >= n_q) return;
-  constexpr int kPer = 2048 / kWave;  // entries per lane at the largest budget
-  const int per = (K + kWave - 1) / kWave;
   const int gpr = R / kRatio;  // groups per range
   const int32_t* row = sel + (size_t)q * K;
   int32_t* o = off + (size_t)q * (NR + 1);
-  int v[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int e = lane * per + i;
-    v[i] = (i < per && e < K) ? row[e] : -1;
-  }
-  // the largest entry of this lane's run (the valid entries are a prefix of
-  // the row, ascending), and the number of valid entries
-  int last = -1, n_valid = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    last = max(last, v[i]);
-    n_valid += v[i] >= 0 ? 1 : 0;
-  }
-#pragma unroll
-  for (int o2 = 32; o2 >= 1; o2 >>= 1) n_valid += __shfl_xor(n_valid, o2, kWave);
-  int prev = __shfl_up(last, 1, kWave);
-  if (lane == 0) prev = -1;
-  int prev_r = prev >= 0 ? prev / gpr : -1;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    if (v[i] >= 0) {
-      const int e = lane * per + i;
-      const int rr = min(v[i] / gpr, NR);
-      for (int b = prev_r + 1; b <= rr; ++b) o[b] = e;
-      prev_r = max(prev_r, rr);
-    }
+  int prev_r = -1;   // range of the entry before this chunk (wave-uniform)
+  int n_valid = 0;   // valid entries so far (a prefix of the row)
+  for (int c0 = 0; c0 < K; c0 += kWave) {
+    const int e = c0 + lane;
+    const int v = e < K ? row[e] : -1;
+    const int rr = v >= 0 ? min(v / gpr, NR) : -1;
+    int before = __shfl_up(rr, 1, kWave);  // range of entry e - 1
+    if (lane == 0) before = prev_r;
+    if (v >= 0)
+      for (int b = max(before, -1) + 1; b <= rr; ++b) o[b] = e;
+    const uint64_t valid = __ballot(v >= 0);
+    n_valid += __popcll(valid);
+    const int last = valid ? 63 - __clzll(valid) : -1;  // last valid lane of the chunk
+    if (last >= 0) prev_r = __shfl(rr, last, kWave);
+    if (valid != ~0ull) break;  // the valid entries have ended
   }
   // boundaries past the last valid entry's range (all of them when the
   // selection is empty)
-  const int last_g = n_valid > 0 ? row[n_valid - 1] : -1;
-  const int last_r = last_g >= 0 ? min(last_g / gpr, NR) : -1;
-  for (int b = last_r + 1 + lane; b <= NR; b += kWave) o[b] = n_valid;
+  for (int b = prev_r + 1 + lane; b <= NR; b += kWave) o[b] = n_valid;
+}
+
+// Merge of the prefill range partials: one workgroup per (query, KV head),
+// thread d owns output dimension d of the KV head's gq query heads;
+// out = sum_r 2^(m_r - M) acc_r / sum_r 2^(m_r - M) l_r over the ranges.
+__global__ __launch_bounds__(kHeadDim) void combine_ranges_kernel(
+    const float* __restrict__ part, int NR, int Hq, int Hkv, float v_scale,
+    float* __restrict__ out) {
+  const int b = blockIdx.x / Hkv, kvh = blockIdx.x - b * Hkv;
+  const int gq = Hq / Hkv, t = threadIdx.x;
+  const float* p = part + ((size_t)b * Hkv + kvh) * NR * gq * kRangePitch;
+  for (int r = 0; r < gq; ++r) {
+    float M = -INFINITY;
+    for (int s = 0; s < NR; ++s) M = fmaxf(M, p[((size_t)s * gq + r) * kRangePitch]);
+    float den = 0.0f, num = 0.0f;
+    for (int s = 0; s < NR; ++s) {
+      const float* row = p + ((size_t)s * gq + r) * kRangePitch;
+      const float m = row[0];
+      const float f = m == -INFINITY ? 0.0f : exp2f(m - M);
+      den += f * row[1];
+      num += f * row[4 + t];
+    }
+    out[((size_t)b * Hq + (size_t)kvh * gq + r) * kHeadDim + t] =
+        den > 0.0f ? num * (v_scale / den) : 0.0f;
+  }
 }
 
 template <bool kFp8>
@@ -721,14 +731,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_ranges_kernel(
 // Merge split partials: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
 // Thread s first fetches split s's (m, l) so all splits are read at once;
 // then thread d sums the accumulators with independent loads.
-// A partial row is `pitch` floats: max, sum, then the accumulator from
-// float `acc_off` on (decode: pitch 2 + 256, offset 2; prefill ranges:
-// 16-byte aligned rows of 260, offset 4).
+// A partial row is 2 + 256 floats: max, sum, then the accumulator.
 constexpr int kMaxSplits = kHeadDim;
 __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restrict__ partial,
                                                            int n_splits, int Hq, int Hkv, int Q,
-                                                           float v_scale, float* __restrict__ out,
-                                                           int pitch, int acc_off) {
+                                                           float v_scale, float* __restrict__ out) {
+  constexpr int pitch = 2 + kHeadDim, acc_off = 2;
   __shared__ float fac[kMaxSplits];
   __shared__ float red[kHeadDim / kWave];
   const int h = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
@@ -805,7 +813,7 @@ hipError_t launch_decode_t(const AttnArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   dim3 cgrid(a.Hq, a.q_per_req, a.batch);
   hipLaunchKernelGGL(combine_kernel, cgrid, dim3(kHeadDim), 0, stream, a.partial, a.n_splits, a.Hq,
-                     a.Hkv, a.q_per_req, a.v_scale, a.out, 2 + kHeadDim, 2);
+                     a.Hkv, a.q_per_req, a.v_scale, a.out);
   return hipGetLastError();
 }
 
@@ -840,9 +848,8 @@ hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
                      dim3(kAttnThreads), smem, stream, a, R, NR, n_qb, a.range_offsets, a.partial);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 cgrid(a.Hq, 1, a.batch);
-  hipLaunchKernelGGL(combine_kernel, cgrid, dim3(kHeadDim), 0, stream, a.partial, NR, a.Hq, a.Hkv,
-                     1, a.v_scale, a.out, kRangePitch, 4);
+  hipLaunchKernelGGL(combine_ranges_kernel, dim3((unsigned)((size_t)a.batch * a.Hkv)),
+                     dim3(kHeadDim), 0, stream, a.partial, NR, a.Hq, a.Hkv, a.v_scale, a.out);
   return hipGetLastError();
 }
 

@@ -96,3 +96,25 @@ def test_mfma_counter_summary_and_digest(tmp_path):
     md = (out / f"mfma_util__{bench.PREFILL_SLUG}.md").read_text()
     # 1,000 cycles per XCD in 1 us: the implied clock column reads 1.00 GHz
     assert "| index_score_mfma_kernel<Form<8, 8, 64> > | 1.0 | 8000 | 1.00 |" in md
+
+
+def test_kernel_trace_summary(tmp_path):
+    # a rocprofv3 kernel_stats.csv of two kernels -> the table in the
+    # committed profile format, sorted by total time, shares summing to 100 %
+    d = tmp_path / "trace" / "host"
+    os.makedirs(d)
+    with open(d / "run_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs",
+                    "MaxNs", "StdDev"])
+        w.writerow(["void qsa::(anonymous namespace)::combine_kernel(float const*, int)", 10,
+                    50000, 5000, 20.0, 4000, 7000, 1.0])
+        w.writerow(["qsa::(anonymous namespace)::index_score_gemv_kernel(float const*)", 2,
+                    200000, 100000, 80.0, 99000, 101000, 1.0])
+    path = bench.write_trace(str(tmp_path / "trace"), ["rocprofv3 ... -- python3 bench.py"],
+                             out_dir=str(tmp_path / "profiles"))
+    text = open(path).read()
+    rows = [l for l in text.splitlines() if l.startswith("| ") and "calls" not in l]
+    assert rows[0].startswith("| index_score_gemv_kernel | 2 | 100.00 | 99.00 | 101.00 | 80.0% |")
+    assert rows[1].startswith("| combine_kernel | 10 | 5.00 | 4.00 | 7.00 | 20.0% |")
+    assert "rocprofv3 ... -- python3 bench.py" in text
