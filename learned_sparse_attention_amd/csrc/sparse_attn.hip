@@ -101,66 +101,91 @@ __device__ __forceinline__ int out_dim(int lg, int i, int mb) {
   return kFp8 ? 16 * r + mb : 8 * r + (mb & 7) + 128 * (mb >> 3);
 }
 
-// Loads one 16-token sub-tile: K rows of the 16 tokens tok[0..16) (physical
-// row offsets, -1 if absent) and the V rows in MFMA operand order.  Each
-// lane's V pieces are read past the caches when kStreamV (decode reads each
-// selected row once).
+// Loads the K part of one 16-token sub-tile: the K rows of tokens
+// tok[0..16) (physical row offsets, -1 if absent; absent rows read row 0).
+// Load i holds bytes 64*i + 16*lg .. +15 of token lq's K row (k-step i for
+// bf16, k-steps 2i and 2i + 1 for fp8).
+template <bool kFp8>
+__device__ __forceinline__ void load_k_rows(u32x4 (&k)[kFp8 ? 4 : 8], const int32_t* tok,
+                                            const uint8_t* kc, int Hkv, int kvh) {
+  const int lane = threadIdx.x & (kWave - 1), lq = lane & 15, lg = lane >> 4;
+  constexpr int kRowBytes = kHeadDim * (kFp8 ? 1 : 2);
+  const uint8_t* kp = kc + ((size_t)max(tok[lq], 0) * Hkv + kvh) * kRowBytes + 16 * lg;
+#pragma unroll
+  for (int i = 0; i < (kFp8 ? 4 : 8); ++i) k[i] = *reinterpret_cast<const u32x4*>(kp + 64 * i);
+}
+
+// Loads the V part of one sub-tile in MFMA operand order: rv[j] = row of
+// token 4*lg + j; fp8: bytes 16*lq .. +15 of its V row, bf16: elements
+// 8*lq + 128*i .. +7 (i = 0, 1).  kStreamV reads past the caches (decode
+// reads each selected row once).
+template <bool kFp8, bool kStreamV>
+__device__ __forceinline__ void load_v_rows(u32x4 (&v)[4][kFp8 ? 1 : 2], int (&rv)[4],
+                                            const int32_t* tok, const uint8_t* vc, int Hkv,
+                                            int kvh) {
+  const int lane = threadIdx.x & (kWave - 1), lq = lane & 15, lg = lane >> 4;
+  constexpr int kRowBytes = kHeadDim * (kFp8 ? 1 : 2);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    rv[j] = tok[4 * lg + j];
+    const uint8_t* vp = vc + ((size_t)max(rv[j], 0) * Hkv + kvh) * kRowBytes + 16 * lq;
+#pragma unroll
+    for (int i = 0; i < (kFp8 ? 1 : 2); ++i)
+      v[j][i] = kStreamV ? stream_load_u4(vp + 256 * i)
+                         : *reinterpret_cast<const u32x4*>(vp + 256 * i);
+  }
+}
+
+// Loads one whole sub-tile, K first.
 template <bool kFp8, bool kStreamV>
 __device__ __forceinline__ void load_subtile(SubTile<kFp8>& b, const int32_t* tok,
                                              const uint8_t* kc, const uint8_t* vc, int Hkv,
                                              int kvh) {
-  const int lane = threadIdx.x & (kWave - 1), lq = lane & 15, lg = lane >> 4;
-  constexpr int kEsize = kFp8 ? 1 : 2;
-  constexpr int kRowBytes = kHeadDim * kEsize;
-  const int rk = tok[lq];
-  // load i: bytes 64*i + 16*lg .. +15 of the K row (k-step i for bf16,
-  // k-steps 2i and 2i + 1 for fp8)
-  const uint8_t* kp = kc + ((size_t)max(rk, 0) * Hkv + kvh) * kRowBytes + 16 * lg;
-#pragma unroll
-  for (int i = 0; i < (kFp8 ? 4 : 8); ++i) b.k[i] = *reinterpret_cast<const u32x4*>(kp + 64 * i);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    b.rv[j] = tok[4 * lg + j];
-    // fp8: bytes 16*lq .. +15; bf16: elements 8*lq + 128*i .. +7 (i = 0, 1)
-    const uint8_t* vp = vc + ((size_t)max(b.rv[j], 0) * Hkv + kvh) * kRowBytes + 16 * lq;
-#pragma unroll
-    for (int i = 0; i < (kFp8 ? 1 : 2); ++i)
-      b.v[j][i] = kStreamV ? stream_load_u4(vp + 256 * i)
-                           : *reinterpret_cast<const u32x4*>(vp + 256 * i);
-  }
+  load_k_rows<kFp8>(b.k, tok, kc, Hkv, kvh);
+  load_v_rows<kFp8, kStreamV>(b.v, b.rv, tok, vc, Hkv, kvh);
 }
 
-// One sub-tile's contribution to the online softmax of the 16 query rows:
-//   S^T = K . Q^T with Q^T operand qop[ks] (row lq, dims qk_dim(ks, lg) + 0..7);
-//   the weights of the visible tokens (vis[i] for D row 4*lg + i) update
-//   the running max m_run, sum l_run and O^T accumulators acc.
+// S^T = K . Q^T of one sub-tile (16 tokens x 16 query rows): k-step ks
+// takes the K operand kop(ks) (token lq, dims qk_dim(ks, lg) + 0..7, as
+// bf16) and the Q^T operand qop(ks) (row lq, the same dims).
+template <typename KOp, typename QOp>
+__device__ __forceinline__ float4_t subtile_logits(KOp kop, QOp qop) {
+  float4_t sc = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop(ks), __builtin_bit_cast(bf16x8, qop(ks)), sc,
+                                                0, 0, 0);
+  return sc;
+}
+
+// The K operand of k-step ks from a sub-tile's K registers (fp8 widened).
 template <bool kFp8>
-__device__ __forceinline__ void subtile_update(SubTile<kFp8>& b, const u32x4 (&qop)[8],
-                                               const bool (&vis)[4], float qk_scale,
-                                               float& m_run, float& l_run, float4_t (&acc)[16]) {
+__device__ __forceinline__ bf16x8 k_operand(const u32x4 (&k)[kFp8 ? 4 : 8], int ks) {
+  if (kFp8) {
+    const u32x4 w = k[ks / 2];
+    return (ks & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
+  }
+  return __builtin_bit_cast(bf16x8, k[ks]);
+}
+
+// The online-softmax update of one sub-tile from its logits sc: the
+// weights of the visible tokens (vis[i] for D row 4*lg + i) update the
+// running max m_run, sum l_run and the O^T accumulators acc with V^T . P^T.
+template <bool kFp8>
+__device__ __forceinline__ void subtile_accumulate(float4_t sc, u32x4 (&v)[4][kFp8 ? 1 : 2],
+                                                   const int (&rv)[4], const bool (&vis)[4],
+                                                   float qk_scale, float& m_run, float& l_run,
+                                                   float4_t (&acc)[16]) {
   // Absent tokens (padding, out-of-range pages) were loaded from row 0 of
   // the cache, which may hold anything: their V operands are cleared so a
   // zero weight cannot meet a NaN.  Nearly every sub-tile is full, so the
   // clearing runs only when the wavefront holds an absent token.
-  if (!__all(b.rv[0] >= 0 && b.rv[1] >= 0 && b.rv[2] >= 0 && b.rv[3] >= 0)) {
+  if (!__all(rv[0] >= 0 && rv[1] >= 0 && rv[2] >= 0 && rv[3] >= 0)) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < (kFp8 ? 1 : 2); ++i)
-        if (b.rv[j] < 0) b.v[j][i] = (u32x4){0u, 0u, 0u, 0u};
-  }
-  float4_t sc = (float4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    bf16x8 kop;
-    if (kFp8) {
-      const u32x4 w = b.k[ks / 2];
-      kop = (ks & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
-    } else {
-      kop = __builtin_bit_cast(bf16x8, b.k[ks]);
-    }
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, __builtin_bit_cast(bf16x8, qop[ks]), sc, 0,
-                                                0, 0);
+        if (rv[j] < 0) v[j][i] = (u32x4){0u, 0u, 0u, 0u};
   }
   float sv[4];
   float tmax = -INFINITY;
@@ -202,11 +227,11 @@ __device__ __forceinline__ void subtile_update(SubTile<kFp8>& b, const u32x4 (&q
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (kFp8) {
-        const u32x4 w = b.v[j][0];
+        const u32x4 w = v[j][0];
         const uint32_t word = qd < 2 ? w.x : qd < 4 ? w.y : qd < 6 ? w.z : w.w;
         cv[j] = (qd & 1) ? fp8x2_to_bf16x2<true>(word) : fp8x2_to_bf16x2<false>(word);
       } else {
-        const u32x4 w = b.v[j][qd / 4];
+        const u32x4 w = v[j][qd / 4];
         const int e = qd % 4;
         cv[j] = e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
       }
@@ -222,6 +247,17 @@ __device__ __forceinline__ void subtile_update(SubTile<kFp8>& b, const u32x4 (&q
       acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, p_lo, acc[mb], 0, 0, 0);
     }
   }
+}
+
+// One sub-tile's contribution to the online softmax of the 16 query rows,
+// with the Q^T operands qop[ks] in registers.
+template <bool kFp8>
+__device__ __forceinline__ void subtile_update(SubTile<kFp8>& b, const u32x4 (&qop)[8],
+                                               const bool (&vis)[4], float qk_scale,
+                                               float& m_run, float& l_run, float4_t (&acc)[16]) {
+  const float4_t sc = subtile_logits([&](int ks) { return k_operand<kFp8>(b.k, ks); },
+                                     [&](int ks) { return qop[ks]; });
+  subtile_accumulate<kFp8>(sc, b.v, b.rv, vis, qk_scale, m_run, l_run, acc);
 }
 
 // One work item: the 16 query rows row_base .. row_base + 15 (row r =
@@ -502,17 +538,30 @@ constexpr int kRangePitch = kHeadDim + 4;  // partial row: max, sum, 2 unused, a
 #define QSA_RANGE_KIB 8192
 #endif
 constexpr int kRangeBytes = QSA_RANGE_KIB << 10;
-// 16-token sub-tiles each wavefront keeps in flight (bf16 K/V; fp8 takes 2).
-#ifndef QSA_BF16_SUBTILES
-#define QSA_BF16_SUBTILES 1
-#endif
 constexpr int kRangeTok = 1024;            // stream entries translated at a time per wavefront
 constexpr int kRangeGpl = kRangeTok / (kRatio * kWave);  // groups per lane per translation step
 
-// Floats of LDS per wavefront: the token rows of one translation step, then
-// (reused) the transposed partial rows of the query's gq heads.
-__host__ __device__ constexpr int range_wave_floats(int gq) {
-  return gq * kRangePitch > kRangeTok + 16 ? gq * kRangePitch : kRangeTok + 16;
+// LDS per wavefront, in floats: the token rows of one translation step,
+// then one sub-tile's K rows (16 tokens x 512 bytes); at the end (reused)
+// the transposed partial rows of the query's heads.
+constexpr int kRangeKFloats = 16 * kHeadDim / 2;
+constexpr int kRangeWaveFloats = kRangeTok + 16 + kRangeKFloats;
+constexpr int kRangeRowsLds = kRangeWaveFloats / kRangePitch;  // partial rows per LDS pass
+static_assert(kRangeRowsLds >= 8, "a pass holds at least 8 partial rows");
+
+// K rows through LDS.  Read straight into MFMA operand order, the 64 lanes
+// of one load instruction would touch 16 different rows with adjacent
+// lanes in different rows, so no four lanes share a 64-byte segment and the
+// vector L1 serves 64 separate accesses per instruction (four times the 16
+// of a load whose lane quads read contiguous 64 bytes; the L1 access rate
+// then bounds the kernel).  Instead lane 4t + c reads bytes 64j + 16c of
+// token t's row in load j (contiguous quads) and stores them to LDS; the
+// operands are read back per k-step.  The 16-byte chunk k of token t's row
+// sits at chunk position k ^ k_swizzle(t) of LDS row t, which keeps both the
+// stores (16 tokens x 4 chunks) and the operand reads (16 tokens, one chunk)
+// free of bank conflicts when the hardware serves 8 or 16 lanes per pass.
+__device__ __forceinline__ int k_swizzle(int t) {
+  return ((t & 1) ? 4 : 0) ^ ((t & 2) ? 9 : 0) ^ ((t & 4) ? 2 : 0) ^ ((t & 8) ? 8 : 0);
 }
 
 // off[q * (NR + 1) + r] = number of entries of query q's selection (ascending
@@ -550,32 +599,51 @@ __global__ __launch_bounds__(kAttnThreads) void range_offsets_kernel(
   for (int b = prev_r + 1 + lane; b <= NR; b += kWave) o[b] = n_valid;
 }
 
-// Merge of the prefill range partials: one workgroup per (query, KV head),
-// thread d owns output dimension d of the KV head's gq query heads;
-// out = sum_r 2^(m_r - M) acc_r / sum_r 2^(m_r - M) l_r over the ranges.
+// Merge of the prefill range partials, one workgroup per (query, KV head):
+// out = sum_r 2^(m_r - M) acc_r / sum_r 2^(m_r - M) l_r over the ranges r.
+// The first gq threads turn each head's (max, sum) pairs into one factor
+// per partial row; then every thread owns four output dimensions of one
+// head at a time, with all of that head's range loads in flight together.
+constexpr int kMaxRanges = 32;
 __global__ __launch_bounds__(kHeadDim) void combine_ranges_kernel(
     const float* __restrict__ part, int NR, int Hq, int Hkv, float v_scale,
     float* __restrict__ out) {
+  __shared__ float fac[kMaxRanges * 16];
   const int b = blockIdx.x / Hkv, kvh = blockIdx.x - b * Hkv;
   const int gq = Hq / Hkv, t = threadIdx.x;
   const float* p = part + ((size_t)b * Hkv + kvh) * NR * gq * kRangePitch;
-  for (int r = 0; r < gq; ++r) {
+  if (t < gq) {
     float M = -INFINITY;
-    for (int s = 0; s < NR; ++s) M = fmaxf(M, p[((size_t)s * gq + r) * kRangePitch]);
-    float den = 0.0f, num = 0.0f;
+    for (int s = 0; s < NR; ++s) M = fmaxf(M, p[((size_t)s * gq + t) * kRangePitch]);
+    float den = 0.0f;
     for (int s = 0; s < NR; ++s) {
-      const float* row = p + ((size_t)s * gq + r) * kRangePitch;
-      const float m = row[0];
-      const float f = m == -INFINITY ? 0.0f : exp2f(m - M);
+      const float* row = p + ((size_t)s * gq + t) * kRangePitch;
+      const float f = row[0] == -INFINITY ? 0.0f : exp2f(row[0] - M);
+      fac[s * gq + t] = f;
       den += f * row[1];
-      num += f * row[4 + t];
     }
-    out[((size_t)b * Hq + (size_t)kvh * gq + r) * kHeadDim + t] =
-        den > 0.0f ? num * (v_scale / den) : 0.0f;
+    // a head with no visible token (den = 0) outputs exact zeros
+    const float sc = den > 0.0f ? v_scale / den : 0.0f;
+    for (int s = 0; s < NR; ++s) fac[s * gq + t] *= sc;
+  }
+  __syncthreads();
+  constexpr int kRowsPerPass = kHeadDim / (kHeadDim / 4);  // 4 heads per pass
+  const int d4 = t % (kHeadDim / 4), r0 = t / (kHeadDim / 4);
+  for (int r = r0; r < gq; r += kRowsPerPass) {
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+    for (int s = 0; s < NR; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(p + ((size_t)s * gq + r) * kRangePitch +
+                                                        4 + 4 * d4);
+      const float f = fac[s * gq + r];
+      num.x += f * v.x; num.y += f * v.y; num.z += f * v.z; num.w += f * v.w;
+    }
+    *reinterpret_cast<float4*>(out + ((size_t)b * Hq + (size_t)kvh * gq + r) * kHeadDim +
+                               4 * d4) = num;
   }
 }
 
-template <bool kFp8>
+// BF16 K/V (rows of 512 bytes).
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_ranges_kernel(
     AttnArgs a, int R, int NR, int n_qb, const int32_t* __restrict__ off,
     float* __restrict__ part) {
@@ -594,8 +662,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_ranges_kernel(
   const int lq = lane & 15, lg = lane >> 4;
   const int q = qb * kAttnWaves + wave;
   if (q >= a.batch) return;  // whole wavefronts; nothing below synchronises the block
-  float* wl = smem + (size_t)wave * range_wave_floats(gq);
+  float* wl = smem + (size_t)wave * kRangeWaveFloats;
   int32_t* tok = reinterpret_cast<int32_t*>(wl);
+  uint8_t* k_lds = reinterpret_cast<uint8_t*>(wl + kRangeTok + 16);
 
   // the query's selected groups and current-block tokens inside the range
   const int L = a.first_pos + q + 1;
@@ -619,10 +688,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_ranges_kernel(
     const uint16_t* qr = a.q + ((size_t)q * a.Hq + (size_t)kvh * gq + min(lq, gq - 1)) * kHeadDim;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qr + qk_dim<kFp8>(ks, lg));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qr + qk_dim<false>(ks, lg));
       qop[ks] = lq < gq ? v : (u32x4){0u, 0u, 0u, 0u};
     }
   }
+  // this lane's K chunks: loads of token lane / 4 (chunks 4j + lane % 4),
+  // stores to LDS row lane / 4, operand reads from LDS row lq
+  const int kt = lane >> 2, kc4 = lane & 3;
+  const int kw_swz = k_swizzle(kt), kr_swz = k_swizzle(lq);
   const float qk_scale = a.sm_scale * a.k_scale * kLog2e;
   float m_run = -INFINITY, l_run = 0.0f;
   float4_t acc[16];
@@ -633,7 +706,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_ranges_kernel(
   const int32_t* pt = a.page_table + (size_t)a.req * a.max_pages;
   const int32_t* srow = a.sel + (size_t)q * a.K + lo;
 
-  constexpr int kNS = kFp8 ? 2 : QSA_BF16_SUBTILES;  // sub-tiles in flight per wavefront
   for (int c0 = 0; c0 < n_stream; c0 += kRangeTok) {
     // stream entries c0 + 4*(u*64 + lane) .. + 3 -> physical rows: a selected
     // group's four tokens (one page), or up to four current-block tokens.
@@ -680,21 +752,39 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_ranges_kernel(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int n_sub = min(kRangeTok / 16, (n_stream - c0 + 15) / 16);
-    for (int s = 0; s < n_sub; s += kNS) {
-      SubTile<kFp8> bt[kNS];
+    for (int s = 0; s < n_sub; ++s) {
+      const int32_t* ts = tok + 16 * s;
+      // K rows with contiguous lane quads, V rows in operand order
+      u32x4 kst[8];
+      {
+        const uint8_t* kp =
+            kc + ((size_t)max(ts[kt], 0) * a.Hkv + kvh) * (kHeadDim * 2) + 16 * kc4;
 #pragma unroll
-      for (int u = 0; u < kNS; ++u)
-        if (s + u < n_sub)
-          load_subtile<kFp8, false>(bt[u], tok + 16 * (s + u), kc, vc, a.Hkv, kvh);
-#pragma unroll
-      for (int u = 0; u < kNS; ++u) {
-        if (s + u < n_sub) {
-          bool vis[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) vis[k] = bt[u].rv[k] >= 0;
-          subtile_update<kFp8>(bt[u], qop, vis, qk_scale, m_run, l_run, acc);
-        }
+        for (int j = 0; j < 8; ++j) kst[j] = *reinterpret_cast<const u32x4*>(kp + 64 * j);
       }
+      u32x4 vr[4][2];
+      int rv[4];
+      load_v_rows<false, false>(vr, rv, ts, vc, a.Hkv, kvh);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<u32x4*>(k_lds + kt * 512 + 16 * ((4 * j + kc4) ^ kw_swz)) = kst[j];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      bool vis[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vis[k] = rv[k] >= 0;
+      const float4_t sc = subtile_logits(
+          [&](int ks) {
+            return *reinterpret_cast<const bf16x8*>(k_lds + lq * 512 +
+                                                    16 * ((4 * ks + lg) ^ kr_swz));
+          },
+          [&](int ks) { return qop[ks]; });
+      subtile_accumulate<false>(sc, vr, rv, vis, qk_scale, m_run, l_run, acc);
+      // the next sub-tile's stores come after these operand reads
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -704,28 +794,34 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_ranges_kernel(
   // ---- the partial rows: row lq's sum over its four lanes, then the
   // accumulator transposed through LDS (acc[mb][i] of lane (lq, lg) is
   // dimension out_dim(lg, i, mb); runs of four consecutive mb are four
-  // consecutive dimensions) and written with 16-byte stores
+  // consecutive dimensions) and written with 16-byte stores, up to
+  // kRangeRowsLds rows at a time
   float l = l_run;
   l += __shfl_xor(l, 16, kWave);
   l += __shfl_xor(l, 32, kWave);
-  if (lq < gq) {
-    float* rowp = wl + lq * kRangePitch;
-    if (lg == 0) *reinterpret_cast<float4*>(rowp) = make_float4(m_run, l, 0.0f, 0.0f);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<float4*>(rowp + 4 + out_dim<kFp8>(lg, i, 4 * c)) =
-            make_float4(acc[4 * c][i], acc[4 * c + 1][i], acc[4 * c + 2][i], acc[4 * c + 3][i]);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   float4* dst = reinterpret_cast<float4*>(part + (((size_t)q * a.Hkv + kvh) * NR + r) * gq *
                                                      kRangePitch);
   const float4* srcl = reinterpret_cast<const float4*>(wl);
-  const int nf4 = gq * (kRangePitch / 4);
-  for (int e = lane; e < nf4; e += kWave) dst[e] = srcl[e];
+  for (int h0 = 0; h0 < gq; h0 += kRangeRowsLds) {
+    if (lq >= h0 && lq < min(gq, h0 + kRangeRowsLds)) {
+      float* rowp = wl + (lq - h0) * kRangePitch;
+      if (lg == 0) *reinterpret_cast<float4*>(rowp) = make_float4(m_run, l, 0.0f, 0.0f);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          *reinterpret_cast<float4*>(rowp + 4 + out_dim<false>(lg, i, 4 * c)) =
+              make_float4(acc[4 * c][i], acc[4 * c + 1][i], acc[4 * c + 2][i], acc[4 * c + 3][i]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int nf4 = (min(gq, h0 + kRangeRowsLds) - h0) * (kRangePitch / 4);
+    for (int e = lane; e < nf4; e += kWave) dst[h0 * (kRangePitch / 4) + e] = srcl[e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
 }
 
 // Merge split partials: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
@@ -830,8 +926,7 @@ hipError_t launch_prefill_per_query(const AttnArgs& a, hipStream_t stream) {
 }
 
 // BF16 K/V: range partitions (attn_prefill_ranges_kernel), then the merge.
-template <bool kFp8>
-hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_prefill_ranges(const AttnArgs& a, hipStream_t stream) {
   if (a.Hq / a.Hkv > 16) return hipErrorInvalidValue;
   if (!a.range_offsets || !a.partial) return hipErrorInvalidValue;
   int R, NR;
@@ -843,8 +938,8 @@ hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int gq = a.Hq / a.Hkv;
   const int np_pad = (NR * a.Hkv + kXcds - 1) / kXcds * kXcds;
-  const size_t smem = sizeof(float) * (size_t)kAttnWaves * range_wave_floats(gq);
-  hipLaunchKernelGGL((attn_prefill_ranges_kernel<kFp8>), dim3((unsigned)((size_t)n_qb * np_pad)),
+  const size_t smem = sizeof(float) * (size_t)kAttnWaves * kRangeWaveFloats;
+  hipLaunchKernelGGL(attn_prefill_ranges_kernel, dim3((unsigned)((size_t)n_qb * np_pad)),
                      dim3(kAttnThreads), smem, stream, a, R, NR, n_qb, a.range_offsets, a.partial);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -859,7 +954,7 @@ hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
 hipError_t dispatch(const AttnArgs& a, hipStream_t stream, bool prefill) {
   if (a.kv_dtype == 1)
     return prefill ? launch_prefill_per_query(a, stream) : launch_decode_t<true>(a, stream);
-  return prefill ? launch_prefill_t<false>(a, stream) : launch_decode_t<false>(a, stream);
+  return prefill ? launch_prefill_ranges(a, stream) : launch_decode_t<false>(a, stream);
 }
 
 }  // namespace
@@ -872,7 +967,7 @@ void prefill_ranges(int kv_dtype, int Hkv, int max_ctx, int* R, int* NR) {
   const int ctx = max(max_ctx, 1);
   int nr = (ctx + r_l2 - 1) / r_l2;
   nr = max(nr, (kXcds + Hkv - 1) / Hkv);
-  nr = min(nr, 32);
+  nr = min(nr, kMaxRanges);
   int r = (ctx + nr - 1) / nr;
   r = (r + kPage - 1) / kPage * kPage;
   *R = r;

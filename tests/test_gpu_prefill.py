@@ -204,10 +204,12 @@ def test_prefill_rows_of_every_length_past_16384_groups(gpu):
     _prefill_check(wl, gpu, rows[::3], score_rows=rows)
 
 
-@pytest.mark.parametrize("hq,hkv", [(16, 2), (24, 2), (12, 1), (6, 1), (3, 1)])
+@pytest.mark.parametrize("hq,hkv", [(16, 2), (24, 2), (12, 1), (6, 1), (3, 1), (16, 1)])
 @pytest.mark.parametrize("n_q,kv", [(1, "fp8"), (257, "bf16")])
 def test_prefill_head_shapes(gpu, hq, hkv, n_q, kv):
-    # the operator suite's local head shapes at 1 and 257 query rows
+    # the operator suite's local head shapes at 1 and 257 query rows, and
+    # the widest group (16 query heads per KV head: the range kernel's
+    # partial rows then take two LDS passes)
     wl = workload.prefill_workload(840 + 7 * hq + hkv + n_q, 2500, n_q, num_q_heads=hq,
                                    num_kv_heads=hkv, kv_dtype=kv, topk_groups=512)
     _prefill_check(wl, gpu, np.arange(n_q))
