@@ -145,6 +145,68 @@ __device__ __forceinline__ void load_subtile(SubTile<kFp8>& b, const int32_t* to
   load_v_rows<kFp8, kStreamV>(b.v, b.rv, tok, vc, Hkv, kvh);
 }
 
+// K rows through LDS (the BF16 prefill range kernel).  Read straight into
+// MFMA operand order, the 64 lanes of one load instruction touch 16
+// different rows with adjacent lanes in different rows, so no four lanes
+// share a 64-byte segment and the vector L1 serves 64 separate accesses per
+// instruction, four times the 16 of a load whose lane quads read contiguous
+// 64 bytes; where the gathers run at L1 rate, that access count bounds
+// them.  Instead lane 4t + c reads bytes 64j + 16c of token t's row in load
+// j (contiguous quads), stores them to a per-wavefront LDS tile, and the
+// operands are read back per k-step.  The 16-byte chunk k of token t's row
+// sits at chunk position k ^ k_swizzle(t) of LDS row t, which keeps the
+// stores (16 tokens x 4 chunks) and the operand reads (16 tokens, one
+// chunk) free of bank conflicts when the hardware serves 8 or 16 lanes per
+// pass.
+__device__ __forceinline__ int k_swizzle(int t) {
+  return ((t & 1) ? 4 : 0) ^ ((t & 2) ? 9 : 0) ^ ((t & 4) ? 2 : 0) ^ ((t & 8) ? 8 : 0);
+}
+
+// Bytes of one sub-tile's K rows in LDS (16 tokens).
+template <bool kFp8>
+__host__ __device__ constexpr int k_tile_bytes() {
+  return 16 * kHeadDim * (kFp8 ? 1 : 2);
+}
+
+// Loads one sub-tile's K rows with contiguous lane quads: load j of lane
+// 4t + c holds bytes 64j + 16c of the row of token tok[t] (-1: row 0).
+template <bool kFp8>
+__device__ __forceinline__ void load_k_quads(u32x4 (&k)[kFp8 ? 4 : 8], const int32_t* tok,
+                                             const uint8_t* kc, int Hkv, int kvh) {
+  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int kRowBytes = kHeadDim * (kFp8 ? 1 : 2);
+  const uint8_t* kp =
+      kc + ((size_t)max(tok[lane >> 2], 0) * Hkv + kvh) * kRowBytes + 16 * (lane & 3);
+#pragma unroll
+  for (int j = 0; j < (kFp8 ? 4 : 8); ++j) k[j] = *reinterpret_cast<const u32x4*>(kp + 64 * j);
+}
+
+// Stores load_k_quads' registers into the wavefront's LDS tile.
+template <bool kFp8>
+__device__ __forceinline__ void store_k_tile(const u32x4 (&k)[kFp8 ? 4 : 8], uint8_t* tile) {
+  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int kRowBytes = kHeadDim * (kFp8 ? 1 : 2);
+  const int t = lane >> 2, c = lane & 3, sw = k_swizzle(t);
+#pragma unroll
+  for (int j = 0; j < (kFp8 ? 4 : 8); ++j)
+    *reinterpret_cast<u32x4*>(tile + t * kRowBytes + 16 * ((4 * j + c) ^ sw)) = k[j];
+}
+
+// The K operand of k-step ks (token lq, dims qk_dim(ks, lg) + 0..7, as
+// bf16) from the LDS tile; sw = k_swizzle(lq).
+template <bool kFp8>
+__device__ __forceinline__ bf16x8 k_operand_lds(const uint8_t* tile, int ks, int lq, int lg,
+                                                int sw) {
+  constexpr int kRowBytes = kHeadDim * (kFp8 ? 1 : 2);
+  if (kFp8) {
+    // chunk 4 (ks / 2) + lg holds dims 64 (ks / 2) + 16 lg .. + 15
+    const u32x4 w =
+        *reinterpret_cast<const u32x4*>(tile + lq * kRowBytes + 16 * ((4 * (ks >> 1) + lg) ^ sw));
+    return (ks & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
+  }
+  return *reinterpret_cast<const bf16x8*>(tile + lq * kRowBytes + 16 * ((4 * ks + lg) ^ sw));
+}
+
 // S^T = K . Q^T of one sub-tile (16 tokens x 16 query rows): k-step ks
 // takes the K operand kop(ks) (token lq, dims qk_dim(ks, lg) + 0..7, as
 // bf16) and the Q^T operand qop(ks) (row lq, the same dims).
@@ -542,27 +604,13 @@ constexpr int kRangeTok = 1024;            // stream entries translated at a tim
 constexpr int kRangeGpl = kRangeTok / (kRatio * kWave);  // groups per lane per translation step
 
 // LDS per wavefront, in floats: the token rows of one translation step,
-// then one sub-tile's K rows (16 tokens x 512 bytes); at the end (reused)
-// the transposed partial rows of the query's heads.
-constexpr int kRangeKFloats = 16 * kHeadDim / 2;
+// then one sub-tile's K tile; at the end (reused) the transposed partial
+// rows of the query's heads.
+constexpr int kRangeKFloats = k_tile_bytes<false>() / 4;  // room for either element type
+
 constexpr int kRangeWaveFloats = kRangeTok + 16 + kRangeKFloats;
 constexpr int kRangeRowsLds = kRangeWaveFloats / kRangePitch;  // partial rows per LDS pass
 static_assert(kRangeRowsLds >= 8, "a pass holds at least 8 partial rows");
-
-// K rows through LDS.  Read straight into MFMA operand order, the 64 lanes
-// of one load instruction would touch 16 different rows with adjacent
-// lanes in different rows, so no four lanes share a 64-byte segment and the
-// vector L1 serves 64 separate accesses per instruction (four times the 16
-// of a load whose lane quads read contiguous 64 bytes; the L1 access rate
-// then bounds the kernel).  Instead lane 4t + c reads bytes 64j + 16c of
-// token t's row in load j (contiguous quads) and stores them to LDS; the
-// operands are read back per k-step.  The 16-byte chunk k of token t's row
-// sits at chunk position k ^ k_swizzle(t) of LDS row t, which keeps both the
-// stores (16 tokens x 4 chunks) and the operand reads (16 tokens, one chunk)
-// free of bank conflicts when the hardware serves 8 or 16 lanes per pass.
-__device__ __forceinline__ int k_swizzle(int t) {
-  return ((t & 1) ? 4 : 0) ^ ((t & 2) ? 9 : 0) ^ ((t & 4) ? 2 : 0) ^ ((t & 8) ? 8 : 0);
-}
 
 // off[q * (NR + 1) + r] = number of entries of query q's selection (ascending
 // group ids, -1 padded) whose group lies below range r (group < r * R / 4),
@@ -643,7 +691,7 @@ __global__ __launch_bounds__(kHeadDim) void combine_ranges_kernel(
   }
 }
 
-// BF16 K/V (rows of 512 bytes).
+template <bool kFp8>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_ranges_kernel(
     AttnArgs a, int R, int NR, int n_qb, const int32_t* __restrict__ off,
     float* __restrict__ part) {
@@ -688,14 +736,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_ranges_kernel(
     const uint16_t* qr = a.q + ((size_t)q * a.Hq + (size_t)kvh * gq + min(lq, gq - 1)) * kHeadDim;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qr + qk_dim<false>(ks, lg));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qr + qk_dim<kFp8>(ks, lg));
       qop[ks] = lq < gq ? v : (u32x4){0u, 0u, 0u, 0u};
     }
   }
-  // this lane's K chunks: loads of token lane / 4 (chunks 4j + lane % 4),
-  // stores to LDS row lane / 4, operand reads from LDS row lq
-  const int kt = lane >> 2, kc4 = lane & 3;
-  const int kw_swz = k_swizzle(kt), kr_swz = k_swizzle(lq);
+  const int kr_swz = k_swizzle(lq);  // this lane's operand reads: LDS row lq
   const float qk_scale = a.sm_scale * a.k_scale * kLog2e;
   float m_run = -INFINITY, l_run = 0.0f;
   float4_t acc[16];
@@ -752,35 +797,29 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_ranges_kernel(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int n_sub = min(kRangeTok / 16, (n_stream - c0 + 15) / 16);
+    // K rows one sub-tile ahead: sub-tile s + 1's loads are issued into the
+    // registers s's rows leave once they are in LDS, so they arrive while s
+    // computes
+    u32x4 kst[kFp8 ? 4 : 8];
+    if (n_sub > 0) load_k_quads<kFp8>(kst, tok, kc, a.Hkv, kvh);
     for (int s = 0; s < n_sub; ++s) {
       const int32_t* ts = tok + 16 * s;
-      // K rows with contiguous lane quads, V rows in operand order
-      u32x4 kst[8];
-      {
-        const uint8_t* kp =
-            kc + ((size_t)max(ts[kt], 0) * a.Hkv + kvh) * (kHeadDim * 2) + 16 * kc4;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) kst[j] = *reinterpret_cast<const u32x4*>(kp + 64 * j);
-      }
-      u32x4 vr[4][2];
+      // V rows in operand order
+      u32x4 vr[4][kFp8 ? 1 : 2];
       int rv[4];
-      load_v_rows<false, false>(vr, rv, ts, vc, a.Hkv, kvh);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<u32x4*>(k_lds + kt * 512 + 16 * ((4 * j + kc4) ^ kw_swz)) = kst[j];
+      load_v_rows<kFp8, false>(vr, rv, ts, vc, a.Hkv, kvh);
+      store_k_tile<kFp8>(kst, k_lds);
+      if (s + 1 < n_sub) load_k_quads<kFp8>(kst, ts + 16, kc, a.Hkv, kvh);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       bool vis[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) vis[k] = rv[k] >= 0;
-      const float4_t sc = subtile_logits(
-          [&](int ks) {
-            return *reinterpret_cast<const bf16x8*>(k_lds + lq * 512 +
-                                                    16 * ((4 * ks + lg) ^ kr_swz));
-          },
-          [&](int ks) { return qop[ks]; });
-      subtile_accumulate<false>(sc, vr, rv, vis, qk_scale, m_run, l_run, acc);
+      const float4_t sc =
+          subtile_logits([&](int ks) { return k_operand_lds<kFp8>(k_lds, ks, lq, lg, kr_swz); },
+                         [&](int ks) { return qop[ks]; });
+      subtile_accumulate<kFp8>(sc, vr, rv, vis, qk_scale, m_run, l_run, acc);
       // the next sub-tile's stores come after these operand reads
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -810,7 +849,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_ranges_kernel(
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          *reinterpret_cast<float4*>(rowp + 4 + out_dim<false>(lg, i, 4 * c)) =
+          *reinterpret_cast<float4*>(rowp + 4 + out_dim<kFp8>(lg, i, 4 * c)) =
               make_float4(acc[4 * c][i], acc[4 * c + 1][i], acc[4 * c + 2][i], acc[4 * c + 3][i]);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -925,7 +964,10 @@ hipError_t launch_prefill_per_query(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// BF16 K/V: range partitions (attn_prefill_ranges_kernel), then the merge.
+// Range partitions (attn_prefill_ranges_kernel), then the merge; taken for
+// BF16 K/V (FP8 measured slower here than the per-query kernel: 1,055 against
+// 983 us per prefill step of the 4,096-query chunk).
+template <bool kFp8>
 hipError_t launch_prefill_ranges(const AttnArgs& a, hipStream_t stream) {
   if (a.Hq / a.Hkv > 16) return hipErrorInvalidValue;
   if (!a.range_offsets || !a.partial) return hipErrorInvalidValue;
@@ -939,7 +981,7 @@ hipError_t launch_prefill_ranges(const AttnArgs& a, hipStream_t stream) {
   const int gq = a.Hq / a.Hkv;
   const int np_pad = (NR * a.Hkv + kXcds - 1) / kXcds * kXcds;
   const size_t smem = sizeof(float) * (size_t)kAttnWaves * kRangeWaveFloats;
-  hipLaunchKernelGGL(attn_prefill_ranges_kernel, dim3((unsigned)((size_t)n_qb * np_pad)),
+  hipLaunchKernelGGL((attn_prefill_ranges_kernel<kFp8>), dim3((unsigned)((size_t)n_qb * np_pad)),
                      dim3(kAttnThreads), smem, stream, a, R, NR, n_qb, a.range_offsets, a.partial);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -954,7 +996,7 @@ hipError_t launch_prefill_ranges(const AttnArgs& a, hipStream_t stream) {
 hipError_t dispatch(const AttnArgs& a, hipStream_t stream, bool prefill) {
   if (a.kv_dtype == 1)
     return prefill ? launch_prefill_per_query(a, stream) : launch_decode_t<true>(a, stream);
-  return prefill ? launch_prefill_ranges(a, stream) : launch_decode_t<false>(a, stream);
+  return prefill ? launch_prefill_ranges<false>(a, stream) : launch_decode_t<false>(a, stream);
 }
 
 }  // namespace
