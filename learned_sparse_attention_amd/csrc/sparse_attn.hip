@@ -154,12 +154,14 @@ __device__ __forceinline__ void load_subtile(SubTile<kFp8>& b, const int32_t* to
 // them.  Instead lane 4t + c reads bytes 64j + 16c of token t's row in load
 // j (contiguous quads), stores them to a per-wavefront LDS tile, and the
 // operands are read back per k-step.  The 16-byte chunk k of token t's row
-// sits at chunk position k ^ k_swizzle(t) of LDS row t, which keeps the
-// stores (16 tokens x 4 chunks) and the operand reads (16 tokens, one
-// chunk) free of bank conflicts when the hardware serves 8 or 16 lanes per
-// pass.
+// sits at chunk position k ^ k_swizzle(t) of LDS row t.  This XOR pattern
+// was picked by measurement (rocprofv3 SQ_LDS_BANK_CONFLICT over probes of
+// all candidate patterns): it leaves both the 16-byte stores (lane 4t + c,
+// chunk 4j + c) and the operand reads (lane lq + 16 lg, chunk 4 ks + lg)
+// without bank conflicts for every j and ks; other patterns that a plain
+// bank model calls conflict-free cost the reads 4 cycles per instruction.
 __device__ __forceinline__ int k_swizzle(int t) {
-  return ((t & 1) ? 4 : 0) ^ ((t & 2) ? 9 : 0) ^ ((t & 4) ? 2 : 0) ^ ((t & 8) ? 8 : 0);
+  return ((t & 1) ? 4 : 0) ^ ((t & 2) ? 1 : 0) ^ ((t & 4) ? 2 : 0) ^ ((t & 8) ? 8 : 0);
 }
 
 // Bytes of one sub-tile's K rows in LDS (16 tokens).
