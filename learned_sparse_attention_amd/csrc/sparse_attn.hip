@@ -209,6 +209,10 @@ __device__ __forceinline__ bf16x8 k_operand_lds(const uint8_t* tile, int ks, int
   return *reinterpret_cast<const bf16x8*>(tile + lq * kRowBytes + 16 * ((4 * ks + lg) ^ sw));
 }
 
+// LDS of one wavefront's K tile in a decode work item (room for either
+// element type)
+constexpr int kItemKBytesPerWave = k_tile_bytes<false>();
+
 // S^T = K . Q^T of one sub-tile (16 tokens x 16 query rows): k-step ks
 // takes the K operand kop(ks) (token lq, dims qk_dim(ks, lg) + 0..7, as
 // bf16) and the Q^T operand qop(ks) (row lq, the same dims).
@@ -326,19 +330,26 @@ __device__ __forceinline__ void subtile_update(SubTile<kFp8>& b, const u32x4 (&q
 
 // One work item: the 16 query rows row_base .. row_base + 15 (row r =
 // position r / gq, head r % gq of the KV head's group; rows >= n_rows are
-// padding) over the item's token stream.  kStreamV: V rows are read past
-// the caches (decode reads each selected row once); prefill keeps them
-// cacheable, since the queries of a chunk share the request's KV rows.
+// padding) over the item's token stream.  kStreamV (decode): V rows are
+// read past the caches (decode reads each selected row once) and K rows go
+// through the wavefronts' LDS tiles at k_lds (kAttnWaves x
+// kItemKBytesPerWave bytes); prefill keeps V cacheable, since the queries
+// of a chunk share the request's KV rows, loads K straight into operand
+// order and takes no K tiles (k_lds unused).
 template <bool kFp8, bool kStreamV>
 __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& it, int kvh,
                                             const uint16_t* q_rows, int q_row_stride,
                                             int row_base, int n_rows, int gq, float* acc_lds,
-                                            float* ml_lds, uint16_t* q_lds, int32_t* tok_row,
-                                            float* out_final, float* out_partial) {
+                                            float* ml_lds, uint16_t* q_lds, uint8_t* k_lds,
+                                            int32_t* tok_row, float* out_final,
+                                            float* out_partial) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int lq = lane & 15, lg = lane >> 4;
-  constexpr int kQPitch = kHeadDim + 8;  // bf16 elements; spreads the 16 rows over LDS banks
+  // bf16 elements (544 bytes): the operand reads of the 16 rows hit every
+  // LDS bank once (measured: a 528-byte pitch costs each read 4 conflict
+  // cycles)
+  constexpr int kQPitch = kHeadDim + 16;
 
   // ---- token stream -> physical row offsets (page * 64 + slot), -1 if absent
   const int n_groups = max(0, it.g_end - it.g_begin);
@@ -429,9 +440,62 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
     subtile_update<kFp8>(b, qop, vis, qk_scale, m_run, l_run, acc);
   };
 
-  // ---- main loop: rounds of kNS sub-tiles per wave (sub-tiles
-  // wave + 4*i); a round issues all of its loads before computing any of
-  // them, so one memory latency covers kNS sub-tiles
+  if constexpr (kStreamV) {
+  // ---- decode main loop, rolling: the wave's sub-tiles wave + 4*i in turn;
+  // the next sub-tile's K rows (contiguous lane quads, staged through this
+  // wave's LDS tile) and V rows are requested before the current one
+  // computes, so each memory latency overlaps a sub-tile of work
+  // (measured: 199.0 -> 197.9 us per decode step of 8 x 262,144 tokens).
+  const int kr_swz = k_swizzle(lq);
+  uint8_t* tile = k_lds + (size_t)wave * kItemKBytesPerWave;
+  u32x4 kst[kFp8 ? 4 : 8];
+  u32x4 vb[2][4][kFp8 ? 1 : 2];
+  int rb[2][4];
+  if (wave < n_sub) {
+    load_k_quads<kFp8>(kst, tok_row + 16 * wave, kc, Hkv, kvh);
+    load_v_rows<kFp8, kStreamV>(vb[0], rb[0], tok_row + 16 * wave, vc, Hkv, kvh);
+  }
+  auto step = [&](int s, u32x4 (&vcur)[4][kFp8 ? 1 : 2], int (&rcur)[4],
+                  u32x4 (&vnext)[4][kFp8 ? 1 : 2], int (&rnext)[4]) {
+    store_k_tile<kFp8>(kst, tile);
+    const int sn = s + kAttnWaves;
+    if (sn < n_sub) {
+      load_k_quads<kFp8>(kst, tok_row + 16 * sn, kc, Hkv, kvh);
+      load_v_rows<kFp8, kStreamV>(vnext, rnext, tok_row + 16 * sn, vc, Hkv, kvh);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    u32x4 qop[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      qop[ks] = *reinterpret_cast<const u32x4*>(q_lds + lq * kQPitch + qk_dim<kFp8>(ks, lg));
+    bool vis[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int si = 16 * s + 4 * lg + i;
+      const int tok = si < 4 * n_groups ? -1 : it.x_begin + (si - 4 * n_groups);  // -1: visible
+      vis[i] = rcur[i] >= 0 && tok < limit;
+    }
+    const float4_t sc =
+        subtile_logits([&](int ks) { return k_operand_lds<kFp8>(tile, ks, lq, lg, kr_swz); },
+                       [&](int ks) { return qop[ks]; });
+    subtile_accumulate<kFp8>(sc, vcur, rcur, vis, qk_scale, m_run, l_run, acc);
+    // the next store to the tile comes after these operand reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  for (int s = wave; s < n_sub; s += 2 * kAttnWaves) {
+    step(s, vb[0], rb[0], vb[1], rb[1]);
+    if (s + kAttnWaves < n_sub) step(s + kAttnWaves, vb[1], rb[1], vb[0], rb[0]);
+  }
+  } else {
+  // ---- prefill main loop: rounds of kNS sub-tiles per wave (sub-tiles
+  // wave + 4*i), K loaded straight into operand order; a round issues all
+  // of its loads before computing any of them, so one memory latency
+  // covers kNS sub-tiles (the rolling loop above measured slower here:
+  // 955 -> 1,023 us per FP8 prefill step of the 4,096-query chunk)
   constexpr int kNS = kFp8 ? 2 : 1;
   for (int s0 = wave; s0 < n_sub; s0 += kNS * kAttnWaves) {
     SubTile<kFp8> bt[kNS];
@@ -441,6 +505,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
 #pragma unroll
     for (int i = 0; i < kNS; ++i)
       if (s0 + i * kAttnWaves < n_sub) compute(bt[i], s0 + i * kAttnWaves);
+  }
   }
 
   // ---- merge the 4 waves.  Each wave publishes its row maxima and sums,
@@ -513,7 +578,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
 // tile and the token rows during the main loop and the per-wave
 // accumulators during the merge (the barrier before the merge writes
 // separates the two uses).
-constexpr int kQLdsElems = 16 * (kHeadDim + 8);
+constexpr int kQLdsElems = 16 * (kHeadDim + 16);
 constexpr int kMlFloats = (kAttnWaves + 1) * 32;
 
 template <bool kFp8>
@@ -528,7 +593,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_decode_kernel(AttnArgs a
   float* ml_lds = smem;
   float* acc_lds = smem + kMlFloats;
   uint16_t* q_lds = reinterpret_cast<uint16_t*>(acc_lds);
-  int32_t* tok_row = reinterpret_cast<int32_t*>(q_lds + kQLdsElems);
+  uint8_t* k_lds = reinterpret_cast<uint8_t*>(q_lds + kQLdsElems);
+  int32_t* tok_row = reinterpret_cast<int32_t*>(k_lds + kAttnWaves * kItemKBytesPerWave);
 
   const int L0 = a.ctx_lens[b];
   const bool valid = L0 >= 0 && L0 <= a.max_ctx - (Q - 1);
@@ -547,7 +613,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_decode_kernel(AttnArgs a
   const uint16_t* q_rows = a.q + ((size_t)b * Q * a.Hq + (size_t)kvh * gq) * kHeadDim;
   float* part = a.partial + (((size_t)b * a.Hkv + kvh) * a.n_splits + split) * n_rows * (2 + kHeadDim);
   attend_item<kFp8, true>(a, it, kvh, q_rows, a.Hq * kHeadDim, rb * 16, n_rows, gq, acc_lds, ml_lds,
-                    q_lds, tok_row, nullptr, part);
+                          q_lds, k_lds, tok_row, nullptr, part);
 }
 
 template <bool kFp8>
@@ -572,8 +638,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs 
   it.base_len = L;
   const uint16_t* q_rows = a.q + ((size_t)qi * a.Hq + (size_t)kvh * gq) * kHeadDim;
   float* outp = a.out + ((size_t)qi * a.Hq + (size_t)kvh * gq) * kHeadDim;
-  attend_item<kFp8, false>(a, it, kvh, q_rows, 0, 0, gq, gq, acc_lds, ml_lds, q_lds, tok_row, outp,
-                    nullptr);
+  attend_item<kFp8, false>(a, it, kvh, q_rows, 0, 0, gq, gq, acc_lds, ml_lds, q_lds, nullptr,
+                           tok_row, outp, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -930,9 +996,10 @@ __global__ void expand_tokens_kernel(const int32_t* __restrict__ sel, int K,
   }
 }
 
-size_t attn_smem_bytes(int stream_cap) {
+size_t attn_smem_bytes(int stream_cap, bool k_tiles) {
   const size_t acc = sizeof(float) * (size_t)kAttnWaves * 16 * kAccPitch;
   const size_t loop = sizeof(uint16_t) * (size_t)kQLdsElems +
+                      (k_tiles ? (size_t)kAttnWaves * kItemKBytesPerWave : 0) +
                       sizeof(int32_t) * (size_t)((stream_cap + 15) / 16 * 16);
   return sizeof(float) * (size_t)kMlFloats + (acc > loop ? acc : loop);
 }
@@ -941,7 +1008,7 @@ template <bool kFp8>
 hipError_t launch_decode_t(const AttnArgs& a, hipStream_t stream) {
   if (a.n_splits > kMaxSplits) return hipErrorInvalidValue;
   const int cap = 4 * a.groups_per_split + 3 + (a.q_per_req - 1);
-  const size_t smem = attn_smem_bytes(cap);
+  const size_t smem = attn_smem_bytes(cap, true);
   const int rows = a.q_per_req * (a.Hq / a.Hkv);
   const int nblk = (rows + 15) / 16;
   dim3 grid(a.n_splits * nblk, a.Hkv, a.batch);
@@ -960,7 +1027,7 @@ hipError_t launch_decode_t(const AttnArgs& a, hipStream_t stream) {
 // prefill step of the 4,096-query chunk against 1,143 us with ranges).
 hipError_t launch_prefill_per_query(const AttnArgs& a, hipStream_t stream) {
   if (a.Hq / a.Hkv > 16) return hipErrorInvalidValue;
-  const size_t smem = attn_smem_bytes(4 * a.K + 3);
+  const size_t smem = attn_smem_bytes(4 * a.K + 3, false);
   dim3 grid(a.batch, a.Hkv);
   hipLaunchKernelGGL((attn_prefill_kernel<true>), grid, dim3(kAttnThreads), smem, stream, a);
   return hipGetLastError();
