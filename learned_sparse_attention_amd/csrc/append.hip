@@ -109,14 +109,16 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a, int kv_blocks
   const long long tok = idx / chunks;  // request r, new token i
   const int c = (int)(idx - tok * chunks);
   const int r = (int)(tok / a.n_tokens), i = (int)(tok - (long long)r * a.n_tokens);
+  // the new values first: their address does not depend on the page, so
+  // they are in flight while the position and the page id are looked up
+  const long long src = tok * a.row_elems + 8 * c;
+  const qsa_u4v kx = stream_load_u4(a.k_new + src);
+  const qsa_u4v vx = stream_load_u4(a.v_new + src);
   const long long t = (long long)a.start_pos[r] + i;
   if (t < 0 || t / kPage >= a.max_pages) return;
   const int32_t p = a.page_table[(long long)a.req_rows[r] * a.max_pages + t / kPage];
   if (p < 0 || p >= a.num_pages) return;
   const long long dst = ((long long)p * kPage + t % kPage) * a.row_elems + 8 * c;
-  const long long src = tok * a.row_elems + 8 * c;
-  const qsa_u4v kx = stream_load_u4(a.k_new + src);
-  const qsa_u4v vx = stream_load_u4(a.v_new + src);
   store8<kFp8>(a.k_cache, dst, kx, a.k_scale);
   store8<kFp8>(a.v_cache, dst, vx, a.v_scale);
 }
@@ -127,6 +129,8 @@ __device__ __forceinline__ void append_khat(const AppendArgs& a, long long idx) 
   const long long slot = idx / kF4;  // request r, slot j
   const int f = (int)(idx - slot * kF4);
   const int r = (int)(slot / a.khat_slots), j = (int)(slot - (long long)r * a.khat_slots);
+  // the new k̂ first (its address does not depend on the page)
+  const float4 v = stream_load(reinterpret_cast<const float4*>(a.khat_new) + slot * kF4 + f);
   const long long s0 = a.start_pos[r];
   const long long g0 = s0 >= 0 ? s0 / kRatio : -((-s0 + kRatio - 1) / kRatio);  // floor
   const long long g = g0 + j, last = g * kRatio + kRatio - 1;
@@ -134,7 +138,6 @@ __device__ __forceinline__ void append_khat(const AppendArgs& a, long long idx) 
   if (g / kGroupsPerPage >= a.max_pages) return;
   const int32_t p = a.page_table[(long long)a.req_rows[r] * a.max_pages + g / kGroupsPerPage];
   if (p < 0 || p >= a.num_pages) return;
-  const float4 v = stream_load(reinterpret_cast<const float4*>(a.khat_new) + slot * kF4 + f);
   reinterpret_cast<float4*>(a.khat_cache)[((long long)p * kGroupsPerPage + g % kGroupsPerPage) *
                                               kF4 + f] = v;
 }
