@@ -659,6 +659,9 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
   __shared__ uint32_t tmp[2 * NW + 1];
   __shared__ float red[2 * NW];
   __shared__ int sh[4];
+  constexpr int kBinRank = kWave;  // boundary-bin candidates ranked directly
+  __shared__ uint32_t bin_key[kBinRank];
+  __shared__ uint32_t bin_grp[kBinRank];
 
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -707,11 +710,63 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
       ck[m] = tid < cnt[m] ? score_key(__uint_as_float(ck[m])) : 0u;
       kmax = max(kmax, cnt[m] > 0 ? kmx[m] : 0u);
     }
-    T = wide_threshold<NT, MC>(ck, gk, kmax, (uint32_t)K, hist, sh, &take_eq);
+    // One 12-bit radix pass over the top bits of key - gk finds the bin of
+    // the K-th key and how many of that bin's keys are taken; the bin
+    // rarely holds more than a few candidates (2 - 7 in 8 x 65,536 N(0,1)
+    // scores), so one wavefront ranks them by (key desc, index asc) instead
+    // of a second pass.  More than kBinRank of them: the full radix
+    // threshold below.
+    bool done = false;
+    const uint32_t span = kmax >= gk ? kmax - gk : 0u;
+    const int nbits = span ? 32 - __clz(span) : 0;
+    if (nbits > 12) {
+      const int sft = nbits - 12;
+      for (int i = tid; i < 4096; i += NT) hist[i] = 0u;
+      if (tid == 0) sh[2] = 0;
+      __syncthreads();
 #pragma unroll
-    for (int m = 0; m < MC; ++m)
-      if (ck[m] >= T && ck[m]) atomicOr(ck[m] > T ? &selmap[cg[m] >> 5] : &eqmap[cg[m] >> 5],
-                                        1u << (cg[m] & 31));
+      for (int m = 0; m < MC; ++m)
+        if (ck[m]) atomicAdd(&hist[((ck[m] - gk) >> sft) & 4095u], 1u);
+      __syncthreads();
+      if (tid < kWave) {
+        uint32_t b, r;
+        wave_find4096(hist, (uint32_t)K, &b, &r);
+        if (tid == 0) { sh[0] = (int)b; sh[1] = (int)r; }
+      }
+      __syncthreads();
+      const uint32_t bb = (uint32_t)sh[0], rem = (uint32_t)sh[1];
+#pragma unroll
+      for (int m = 0; m < MC; ++m) {
+        if (ck[m] && ((ck[m] - gk) >> sft) == bb) {
+          const int pos = atomicAdd(&sh[2], 1);
+          if (pos < kBinRank) { bin_key[pos] = ck[m]; bin_grp[pos] = cg[m]; }
+        }
+      }
+      __syncthreads();
+      const int nm = sh[2];
+      if (nm <= kBinRank) {
+#pragma unroll
+        for (int m = 0; m < MC; ++m)
+          if (ck[m] && ((ck[m] - gk) >> sft) > bb) atomicOr(&selmap[cg[m] >> 5], 1u << (cg[m] & 31));
+        if (tid < nm) {
+          const uint32_t mk = bin_key[tid], mg = bin_grp[tid];
+          uint32_t rank = 0;
+          for (int j = 0; j < nm; ++j) {
+            const uint32_t kj = bin_key[j];
+            rank += (kj > mk || (kj == mk && bin_grp[j] < mg)) ? 1u : 0u;
+          }
+          if (rank < rem) atomicOr(&selmap[mg >> 5], 1u << (mg & 31));
+        }
+        done = true;
+      }
+    }
+    if (!done) {
+      T = wide_threshold<NT, MC>(ck, gk, kmax, (uint32_t)K, hist, sh, &take_eq);
+#pragma unroll
+      for (int m = 0; m < MC; ++m)
+        if (ck[m] >= T && ck[m]) atomicOr(ck[m] > T ? &selmap[cg[m] >> 5] : &eqmap[cg[m] >> 5],
+                                          1u << (cg[m] & 31));
+    }
   } else {
     // the pruning guess missed: exact ranking of the whole row
     T = exact_threshold_stream<NT>(srow, G, (uint32_t)K, hist, red, sh, &take_eq);
