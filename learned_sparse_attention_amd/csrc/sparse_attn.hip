@@ -38,7 +38,14 @@ namespace {
 
 constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = kAttnThreads / kWave;
-constexpr int kAccPitch = kHeadDim + 1;  // LDS row pitch of the merged accumulator
+// LDS rows of the merged accumulator: dimension d of a row sits at float
+// acc_col(d) = d + d / 64 of a 260-float row.  A wavefront stores the
+// accumulators of one (i, mb) pair at once, lane (lq, lg) writing
+// dimension out_dim(lg, i, mb) of row lq; with the pitch = 4 (mod 64) and
+// the skew, the 64 lanes of an FP8 store land on 64 different banks (a
+// 257-float pitch put the four lane groups on one bank).
+constexpr int kAccPitch = kHeadDim + 4;
+__device__ __forceinline__ int acc_col(int d) { return d + (d >> 6); }
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -532,7 +539,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
 #pragma unroll
       for (int mb = 0; mb < 16; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rowp[out_dim<kFp8>(lg, i, mb)] = acc[mb][i] * fac;
+        for (int i = 0; i < 4; ++i) rowp[acc_col(out_dim<kFp8>(lg, i, mb))] = acc[mb][i] * fac;
     }
   }
   // row statistics: common max and the sum of the rescaled row sums
@@ -558,7 +565,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
     const int r = e / kHeadDim, d = e % kHeadDim;
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) v += acc_lds[((size_t)w * 16 + r) * kAccPitch + d];
+    for (int w = 0; w < kAttnWaves; ++w) v += acc_lds[((size_t)w * 16 + r) * kAccPitch + acc_col(d)];
     const int rg = row_base + r;
     if (out_final) {
       const float Lsum = ml_lds[kAttnWaves * 32 + 16 + r];
