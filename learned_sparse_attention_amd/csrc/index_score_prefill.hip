@@ -88,16 +88,6 @@ __device__ __forceinline__ u32x2 pack4_bf16(float4 a) {
   return (u32x2){__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
 }
 
-// 8 fp32 -> 8 bf16 (round to nearest even), as one 16-byte operand.
-__device__ __forceinline__ u32x4 pack8_bf16(float4 a, float4 b) {
-  const bf16x2_t p0 = {(__bf16)a.x, (__bf16)a.y};
-  const bf16x2_t p1 = {(__bf16)a.z, (__bf16)a.w};
-  const bf16x2_t p2 = {(__bf16)b.x, (__bf16)b.y};
-  const bf16x2_t p3 = {(__bf16)b.z, (__bf16)b.w};
-  return (u32x4){__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                 __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
-}
-
 template <class F>
 __global__ __launch_bounds__(kPfThreads, 1) void index_score_mfma_kernel(
     const float* __restrict__ khat, const int32_t* __restrict__ page_table, int max_pages,

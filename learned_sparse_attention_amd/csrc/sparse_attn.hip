@@ -1054,7 +1054,6 @@ hipError_t launch_prefill_ranges(const AttnArgs& a, hipStream_t stream) {
                      a.batch, R, NR, a.range_offsets);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int gq = a.Hq / a.Hkv;
   const int np_pad = (NR * a.Hkv + kXcds - 1) / kXcds * kXcds;
   const size_t smem = sizeof(float) * (size_t)kAttnWaves * kRangeWaveFloats;
   hipLaunchKernelGGL((attn_prefill_ranges_kernel<kFp8>), dim3((unsigned)((size_t)n_qb * np_pad)),
