@@ -18,12 +18,15 @@
 //   online softmax per query row (exp2 domain, fp32)
 //   O^T[256 x 16 rows]   += V^T[256 x 16 tok] . P^T   (2 x 16 x mfma 16x16x16 bf16,
 //                                                      P as a bf16 hi + lo pair)
-// K and V go from HBM to registers already in MFMA operand order: lane l
-// reads 64 contiguous bytes of token l%16's K row and 16 contiguous bytes
-// of four V rows, so no LDS staging or transposition is needed; FP8 E4M3
-// elements are widened to bf16 exactly by the hardware converter and the
-// per-tensor scales are folded into the logit scale and the final output.
-// The contraction dimension is permuted consistently between the two MFMA
+// V goes from HBM to registers already in MFMA operand order (16 lanes
+// read 256 contiguous bytes of one token's row).  K is either loaded the
+// same way (prefill over FP8 caches: lane l reads 64 bytes of token l%16's
+// row per instruction) or, in decode and the BF16 range kernel, loaded
+// with contiguous lane quads into a per-wavefront LDS tile and read back
+// as operands (see the K-through-LDS helpers).  FP8 E4M3 elements are
+// widened to bf16 exactly by the hardware converter and the per-tensor
+// scales are folded into the logit scale and the final output.  The
+// contraction dimension is permuted consistently between the two MFMA
 // operands (dot products do not depend on the order of d), which is what
 // makes those contiguous loads possible.  Waves merge their (max, sum,
 // accumulator) through LDS at the end.  Decode splits the selection over
