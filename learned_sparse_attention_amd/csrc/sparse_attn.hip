@@ -598,8 +598,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_decode_kernel(AttnArgs a
   const int Q = a.q_per_req;
   const int n_rows = Q * gq;
   const int nblk = (n_rows + 15) / 16;
-  const int split = blockIdx.x / nblk, rb = blockIdx.x % nblk;
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  // workgroup id -> request b = id % batch first: workgroups are dealt to
+  // the XCDs round-robin, so with 8 | batch request b's workgroups run on
+  // the XCD where the top-K wrote its selection (measured: 4 x 3 MTP
+  // positions 78.2 -> 76.7 us per step; 8 x 262,144 tokens unchanged)
+  const int b = blockIdx.x % a.batch, rest = blockIdx.x / a.batch;
+  const int per_kvh = a.n_splits * nblk;
+  const int kvh = rest / per_kvh, sr = rest - kvh * per_kvh;
+  const int split = sr / nblk, rb = sr % nblk;
   float* ml_lds = smem;
   float* acc_lds = smem + kMlFloats;
   uint16_t* q_lds = reinterpret_cast<uint16_t*>(acc_lds);
@@ -952,7 +958,10 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restri
   constexpr int pitch = 2 + kHeadDim, acc_off = 2;
   __shared__ float fac[kMaxSplits];
   __shared__ float red[kHeadDim / kWave];
-  const int h = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  // request first, as the attention workgroups that wrote the partials
+  const int B = gridDim.x / (Hq * Q);
+  const int b = blockIdx.x % B, rest = blockIdx.x / B;
+  const int h = rest % Hq, j = rest / Hq;
   const int gq = Hq / Hkv, kvh = h / gq, r = j * gq + (h % gq);
   const int R = Q * gq;
   const size_t split_stride = (size_t)R * pitch;
@@ -1021,11 +1030,11 @@ hipError_t launch_decode_t(const AttnArgs& a, hipStream_t stream) {
   const size_t smem = attn_smem_bytes(cap, true);
   const int rows = a.q_per_req * (a.Hq / a.Hkv);
   const int nblk = (rows + 15) / 16;
-  dim3 grid(a.n_splits * nblk, a.Hkv, a.batch);
+  dim3 grid(a.n_splits * nblk * a.Hkv * a.batch);
   hipLaunchKernelGGL((attn_decode_kernel<kFp8>), grid, dim3(kAttnThreads), smem, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 cgrid(a.Hq, a.q_per_req, a.batch);
+  dim3 cgrid(a.Hq * a.q_per_req * a.batch);
   hipLaunchKernelGGL(combine_kernel, cgrid, dim3(kHeadDim), 0, stream, a.partial, a.n_splits, a.Hq,
                      a.Hkv, a.q_per_req, a.v_scale, a.out);
   return hipGetLastError();
