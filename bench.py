@@ -272,9 +272,8 @@ def write_trace(trace_dir: str, commands: list, out_dir: str = None) -> str:
              "step (one `qsa_decode`: index_score_gemv_kernel, topk_extract_kernel, "
              "topk_finish_kernel, attn_decode_kernel, combine_kernel), the indexer GEMV alone, "
              "the prefill scoring alone and whole `qsa_prefill` steps on the 4,096-query chunk "
-             "(BF16: index_score_mfma_kernel, topk_row_kernel, range_offsets_kernel, "
-             "attn_prefill_ranges_kernel, combine_ranges_kernel; FP8: attn_prefill_kernel in place of "
-             "the range kernels), the cache append, and the multi-query indexer legs "
+             "(index_score_mfma_kernel, topk_row_kernel, attn_prefill_kernel; BF16 and FP8 K/V), "
+             "the cache append, and the multi-query indexer legs "
              "(`Form<4, 1, 128>` is the shared-key form, `Form<8, 8, 64>` the per-head form).", "",
              "| kernel | calls | average | min | max | share |", "|---|---|---|---|---|---|"]
     for r in rows:
@@ -356,7 +355,7 @@ def prefill_scoring(dev, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / n_step
     del d, sc, out, ws
-    # the same chunk with FP8 E4M3 K/V (its attention takes the per-query kernel)
+    # the same chunk with FP8 E4M3 K/V
     wf = workload.prefill_workload(workload.CONFIG_SEED + 4, 28672, 4096, kv_dtype="fp8",
                                    topk_groups=512)
     df = workload.to_device(wf, dev)

@@ -100,24 +100,6 @@ RowsLayout rows_layout(const qsa_geometry* g, int n_rows, int max_ctx) {
   return r;
 }
 
-// qsa_prefill: the rows layout (scores, sample, selection, top-K scratch),
-// then the attention's range offsets and per-range partials
-struct PrefillLayout {
-  RowsLayout rows;
-  size_t off_ranges, off_partial, total;
-};
-
-PrefillLayout prefill_layout(const qsa_geometry* g, int n_q, int max_ctx) {
-  PrefillLayout p;
-  p.rows = rows_layout(g, n_q, max_ctx);
-  size_t off_bytes = 0;
-  const size_t attn = prefill_attn_workspace_bytes(g->kv_dtype, g->num_q_heads, g->num_kv_heads,
-                                                   n_q, max_ctx, &off_bytes);
-  p.off_ranges = p.rows.total;
-  p.off_partial = p.off_ranges + off_bytes;
-  p.total = align_up(p.rows.total + attn);
-  return p;
-}
 
 bool cache_ok(const qsa_paged_cache* c, bool need_kv) {
   if (!c || !c->khat || !c->page_table || c->max_pages <= 0 || c->num_pages <= 0) return false;
@@ -240,7 +222,7 @@ size_t qsa_decode_workspace_size(const qsa_geometry* g, int32_t batch, int32_t q
 
 size_t qsa_prefill_workspace_size(const qsa_geometry* g, int32_t n_q, int32_t max_ctx) {
   if (qsa_validate(g) != QSA_OK || n_q < 0 || max_ctx < 1 || max_ctx > kCapacity) return 0;
-  return prefill_layout(g, n_q, max_ctx).total;
+  return rows_layout(g, n_q, max_ctx).total;
 }
 
 qsa_status qsa_index_score(const qsa_geometry* g, const qsa_paged_cache* cache, int32_t n_rows,
@@ -360,9 +342,8 @@ qsa_status qsa_prefill(const qsa_geometry* g, const qsa_paged_cache* cache, int3
   if (n_q == 0) return QSA_OK;
   if (!q_idx || !w_idx || !q || !out) return QSA_ERR_INVALID_ARG;
   const int max_ctx = (int)total;
-  const PrefillLayout play = prefill_layout(g, n_q, max_ctx);
-  const RowsLayout& lay = play.rows;
-  if ((st = ws_ok(ws, ws_bytes, play.total)) != QSA_OK) return st;
+  const RowsLayout lay = rows_layout(g, n_q, max_ctx);
+  if ((st = ws_ok(ws, ws_bytes, lay.total)) != QSA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
   float* scores = out_scores ? out_scores : (float*)(w + lay.off_scores);
@@ -381,8 +362,6 @@ qsa_status qsa_prefill(const qsa_geometry* g, const qsa_paged_cache* cache, int3
   a.q = q;
   a.batch = n_q;
   a.out = out;
-  a.range_offsets = (int32_t*)(w + play.off_ranges);
-  a.partial = (float*)(w + play.off_partial);
   QSA_HIP(launch_sparse_attn_prefill(a, s));
   if (out_tokens)
     QSA_HIP(launch_expand_tokens(sel, g->topk_groups, n_q, 1, nullptr, first_pos, max_ctx,

@@ -64,19 +64,12 @@ struct AttnArgs {
   int batch;            // decode: requests; prefill: queries
   int groups_per_split; // decode split size (groups)
   int n_splits;
-  float* partial;  // decode: [B, Hkv, n_splits, Q*Hq/Hkv, 2 + D];
-                   // prefill: [n_q, Hkv, ranges, Hq/Hkv, 4 + D]
-  int32_t* range_offsets;  // prefill: [n_q, ranges + 1] (workspace)
+  float* partial;  // decode: [B, Hkv, n_splits, Q*Hq/Hkv, 2 + D] (workspace)
   float* out;      // prefill: [n_q, Hq, D]; decode: [B, Q, Hq, D] (combine)
 };
 
 hipError_t launch_sparse_attn_decode(const AttnArgs& a, hipStream_t stream);
-// Prefill attention works on token ranges of R tokens (NR of them up to
-// max_ctx); its workspace holds per-query range offsets (the first
-// *off_bytes bytes, 256-byte aligned) and then the per-range partials.
-void prefill_ranges(int kv_dtype, int Hkv, int max_ctx, int* R, int* NR);
-size_t prefill_attn_workspace_bytes(int kv_dtype, int Hq, int Hkv, int n_q, int max_ctx,
-                                    size_t* off_bytes);
+// Prefill attention needs no workspace: it writes the output rows directly.
 hipError_t launch_sparse_attn_prefill(const AttnArgs& a, hipStream_t stream);
 
 // Cache append: K/V of n_tokens new tokens per request (bf16 in, stored in

@@ -9,30 +9,29 @@
 // reads KV head h / (Hq / Hkv); a row with no visible token yields zeros
 // (OrcaRouter article on SGLang PR #41855, zero-output convention).
 //
-// One workgroup (4 wavefronts) owns one work item: a KV head, a slice of the
-// selection list and the query rows that share it (the GQA heads of one
-// query, or of every draft position of a request).  The item's token
-// stream is translated once into physical row offsets in LDS; then each
-// wavefront walks 16-token sub-tiles of it:
+// Decode: one workgroup (4 wavefronts) owns one work item: a KV head, a
+// slice of the selection list and the query rows that share it (the GQA
+// heads of one query, or of every draft position of a request).  The
+// item's token stream is translated once into physical row offsets in LDS;
+// then each wavefront walks 16-token sub-tiles of it:
 //   S^T[16 tok x 16 rows] = K[16 tok x 256] . Q^T     (8 x mfma 16x16x32 bf16)
 //   online softmax per query row (exp2 domain, fp32)
 //   O^T[256 x 16 rows]   += V^T[256 x 16 tok] . P^T   (2 x 16 x mfma 16x16x16 bf16,
 //                                                      P as a bf16 hi + lo pair)
+// Waves merge their (max, sum, accumulator) through LDS, and combine_kernel
+// merges the partials of the workgroups the selection is split over.
+// Prefill: one wavefront per (query, KV head) walks the query's whole
+// selection with the same sub-tile step and writes normalised rows.
+//
 // V goes from HBM to registers already in MFMA operand order (16 lanes
-// read 256 contiguous bytes of one token's row).  K is either loaded the
-// same way (prefill over FP8 caches: lane l reads 64 bytes of token l%16's
-// row per instruction) or, in decode and the BF16 range kernel, loaded
-// with contiguous lane quads into a per-wavefront LDS tile and read back
-// as operands (see the K-through-LDS helpers).  FP8 E4M3 elements are
-// widened to bf16 exactly by the hardware converter and the per-tensor
-// scales are folded into the logit scale and the final output.  The
-// contraction dimension is permuted consistently between the two MFMA
-// operands (dot products do not depend on the order of d), which is what
-// makes those contiguous loads possible.  Waves merge their (max, sum,
-// accumulator) through LDS at the end.  Decode splits the selection over
-// several workgroups and writes (max, sum, accumulator) partials that
-// combine_kernel merges.  Prefill over FP8 caches writes normalised rows
-// directly; over BF16 caches it works in token-range partitions (below).
+// read 256 contiguous bytes of one token's row).  K is loaded with
+// contiguous lane quads into a per-wavefront LDS tile and read back as
+// operands (see the K-through-LDS helpers).  FP8 E4M3 elements are widened
+// to bf16 exactly by the hardware converter and the per-tensor scales are
+// folded into the logit scale and the final output.  The contraction
+// dimension is permuted consistently between the two MFMA operands (dot
+// products do not depend on the order of d), which is what makes those
+// contiguous loads possible.
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
@@ -72,15 +71,9 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Registers of one 16-token sub-tile in flight: lane l holds 64 (fp8) /
-// 128 (bf16) K bytes of token lq = l % 16, and 16 / 32 bytes of the V rows
-// of tokens 4*lg + j (lg = l / 16).
-//
 // Dimension order.  A dot product does not depend on the order of its terms,
 // so the contraction index of S^T = K . Q^T is permuted identically in both
-// operands, chosen so that the four lanes of one token read 64 contiguous
-// bytes of its K row in each load instruction (16 cache lines per
-// instruction rather than 64): in k-step ks, lane group lg supplies
+// operands; in k-step ks, lane group lg supplies
 //   bf16 K: d = 32*ks + 8*lg + 0..7,
 //   fp8 K:  d = 64*(ks/2) + 16*lg + 8*(ks%2) + 0..7 (one 16-byte load
 //           serves two k-steps).
@@ -91,13 +84,6 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 //   fp8 V:  dv = 16*lq + mb (one load of the whole 256-byte row);
 // so accumulator acc[mb][i] of lane (lq, lg) holds output dimension
 // dv(4*lg + i, mb) of query row lq (out_dim below).
-template <bool kFp8>
-struct SubTile {
-  u32x4 k[kFp8 ? 4 : 8];
-  u32x4 v[4][kFp8 ? 1 : 2];
-  int rv[4];  // physical rows of the four V tokens (-1: absent)
-};
-
 // First of the 8 dimensions that k-step ks of lane group lg covers.
 template <bool kFp8>
 __device__ __forceinline__ int qk_dim(int ks, int lg) {
@@ -109,20 +95,6 @@ template <bool kFp8>
 __device__ __forceinline__ int out_dim(int lg, int i, int mb) {
   const int r = 4 * lg + i;
   return kFp8 ? 16 * r + mb : 8 * r + (mb & 7) + 128 * (mb >> 3);
-}
-
-// Loads the K part of one 16-token sub-tile: the K rows of tokens
-// tok[0..16) (physical row offsets, -1 if absent; absent rows read row 0).
-// Load i holds bytes 64*i + 16*lg .. +15 of token lq's K row (k-step i for
-// bf16, k-steps 2i and 2i + 1 for fp8).
-template <bool kFp8>
-__device__ __forceinline__ void load_k_rows(u32x4 (&k)[kFp8 ? 4 : 8], const int32_t* tok,
-                                            const uint8_t* kc, int Hkv, int kvh) {
-  const int lane = threadIdx.x & (kWave - 1), lq = lane & 15, lg = lane >> 4;
-  constexpr int kRowBytes = kHeadDim * (kFp8 ? 1 : 2);
-  const uint8_t* kp = kc + ((size_t)max(tok[lq], 0) * Hkv + kvh) * kRowBytes + 16 * lg;
-#pragma unroll
-  for (int i = 0; i < (kFp8 ? 4 : 8); ++i) k[i] = *reinterpret_cast<const u32x4*>(kp + 64 * i);
 }
 
 // Loads the V part of one sub-tile in MFMA operand order: rv[j] = row of
@@ -146,16 +118,7 @@ __device__ __forceinline__ void load_v_rows(u32x4 (&v)[4][kFp8 ? 1 : 2], int (&r
   }
 }
 
-// Loads one whole sub-tile, K first.
-template <bool kFp8, bool kStreamV>
-__device__ __forceinline__ void load_subtile(SubTile<kFp8>& b, const int32_t* tok,
-                                             const uint8_t* kc, const uint8_t* vc, int Hkv,
-                                             int kvh) {
-  load_k_rows<kFp8>(b.k, tok, kc, Hkv, kvh);
-  load_v_rows<kFp8, kStreamV>(b.v, b.rv, tok, vc, Hkv, kvh);
-}
-
-// K rows through LDS (the BF16 prefill range kernel).  Read straight into
+// K rows through LDS.  Read straight into
 // MFMA operand order, the 64 lanes of one load instruction touch 16
 // different rows with adjacent lanes in different rows, so no four lanes
 // share a 64-byte segment and the vector L1 serves 64 separate accesses per
@@ -219,8 +182,7 @@ __device__ __forceinline__ bf16x8 k_operand_lds(const uint8_t* tile, int ks, int
   return *reinterpret_cast<const bf16x8*>(tile + lq * kRowBytes + 16 * ((4 * ks + lg) ^ sw));
 }
 
-// LDS of one wavefront's K tile in a decode work item (room for either
-// element type)
+// LDS of one wavefront's K tile (room for either element type)
 constexpr int kItemKBytesPerWave = k_tile_bytes<false>();
 
 // S^T = K . Q^T of one sub-tile (16 tokens x 16 query rows): k-step ks
@@ -234,16 +196,6 @@ __device__ __forceinline__ float4_t subtile_logits(KOp kop, QOp qop) {
     sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop(ks), __builtin_bit_cast(bf16x8, qop(ks)), sc,
                                                 0, 0, 0);
   return sc;
-}
-
-// The K operand of k-step ks from a sub-tile's K registers (fp8 widened).
-template <bool kFp8>
-__device__ __forceinline__ bf16x8 k_operand(const u32x4 (&k)[kFp8 ? 4 : 8], int ks) {
-  if (kFp8) {
-    const u32x4 w = k[ks / 2];
-    return (ks & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
-  }
-  return __builtin_bit_cast(bf16x8, k[ks]);
 }
 
 // The online-softmax update of one sub-tile from its logits sc: the
@@ -327,32 +279,19 @@ __device__ __forceinline__ void subtile_accumulate(float4_t sc, u32x4 (&v)[4][kF
   }
 }
 
-// One sub-tile's contribution to the online softmax of the 16 query rows,
-// with the Q^T operands qop[ks] in registers.
-template <bool kFp8>
-__device__ __forceinline__ void subtile_update(SubTile<kFp8>& b, const u32x4 (&qop)[8],
-                                               const bool (&vis)[4], float qk_scale,
-                                               float& m_run, float& l_run, float4_t (&acc)[16]) {
-  const float4_t sc = subtile_logits([&](int ks) { return k_operand<kFp8>(b.k, ks); },
-                                     [&](int ks) { return qop[ks]; });
-  subtile_accumulate<kFp8>(sc, b.v, b.rv, vis, qk_scale, m_run, l_run, acc);
-}
 
-// One work item: the 16 query rows row_base .. row_base + 15 (row r =
-// position r / gq, head r % gq of the KV head's group; rows >= n_rows are
-// padding) over the item's token stream.  kStreamV (decode): V rows are
-// read past the caches (decode reads each selected row once) and K rows go
-// through the wavefronts' LDS tiles at k_lds (kAttnWaves x
-// kItemKBytesPerWave bytes); prefill keeps V cacheable, since the queries
-// of a chunk share the request's KV rows, loads K straight into operand
-// order and takes no K tiles (k_lds unused).
-template <bool kFp8, bool kStreamV>
+// One decode work item: the 16 query rows row_base .. row_base + 15 (row
+// r = position r / gq, head r % gq of the KV head's group; rows >= n_rows
+// are padding) over the item's token stream, written as (max, sum,
+// accumulator) partial rows.  V rows are read past the caches (decode
+// reads each selected row once); K rows go through the wavefronts' LDS
+// tiles at k_lds (kAttnWaves x kItemKBytesPerWave bytes).
+template <bool kFp8>
 __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& it, int kvh,
                                             const uint16_t* q_rows, int q_row_stride,
                                             int row_base, int n_rows, int gq, float* acc_lds,
                                             float* ml_lds, uint16_t* q_lds, uint8_t* k_lds,
-                                            int32_t* tok_row, float* out_final,
-                                            float* out_partial) {
+                                            int32_t* tok_row, float* out_partial) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int lq = lane & 15, lg = lane >> 4;
@@ -429,29 +368,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
   const uint8_t* vc = reinterpret_cast<const uint8_t*>(a.v);
   const int Hkv = a.Hkv;
 
-  auto load = [&](SubTile<kFp8>& b, int s) {
-    load_subtile<kFp8, kStreamV>(b, tok_row + 16 * s, kc, vc, Hkv, kvh);
-  };
-
-  auto compute = [&](SubTile<kFp8>& b, int s) {
-    // Q operand from LDS: row lq, dims qk_dim(ks, lg) + 0..7
-    u32x4 qop[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      qop[ks] = *reinterpret_cast<const u32x4*>(q_lds + lq * kQPitch + qk_dim<kFp8>(ks, lg));
-    // token of D row 4*lg + i is stream entry 16s + 4*lg + i (= V token i)
-    bool vis[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int si = 16 * s + 4 * lg + i;
-      const int tok = si < 4 * n_groups ? -1 : it.x_begin + (si - 4 * n_groups);  // -1: visible
-      vis[i] = b.rv[i] >= 0 && tok < limit;
-    }
-    subtile_update<kFp8>(b, qop, vis, qk_scale, m_run, l_run, acc);
-  };
-
-  if constexpr (kStreamV) {
-  // ---- decode main loop, rolling: the wave's sub-tiles wave + 4*i in turn;
+  // ---- main loop, rolling: the wave's sub-tiles wave + 4*i in turn;
   // the next sub-tile's K rows (contiguous lane quads, staged through this
   // wave's LDS tile) and V rows are requested before the current one
   // computes, so each memory latency overlaps a sub-tile of work
@@ -463,7 +380,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
   int rb[2][4];
   if (wave < n_sub) {
     load_k_quads<kFp8>(kst, tok_row + 16 * wave, kc, Hkv, kvh);
-    load_v_rows<kFp8, kStreamV>(vb[0], rb[0], tok_row + 16 * wave, vc, Hkv, kvh);
+    load_v_rows<kFp8, true>(vb[0], rb[0], tok_row + 16 * wave, vc, Hkv, kvh);
   }
   auto step = [&](int s, u32x4 (&vcur)[4][kFp8 ? 1 : 2], int (&rcur)[4],
                   u32x4 (&vnext)[4][kFp8 ? 1 : 2], int (&rnext)[4]) {
@@ -471,7 +388,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
     const int sn = s + kAttnWaves;
     if (sn < n_sub) {
       load_k_quads<kFp8>(kst, tok_row + 16 * sn, kc, Hkv, kvh);
-      load_v_rows<kFp8, kStreamV>(vnext, rnext, tok_row + 16 * sn, vc, Hkv, kvh);
+      load_v_rows<kFp8, true>(vnext, rnext, tok_row + 16 * sn, vc, Hkv, kvh);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -499,23 +416,6 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
   for (int s = wave; s < n_sub; s += 2 * kAttnWaves) {
     step(s, vb[0], rb[0], vb[1], rb[1]);
     if (s + kAttnWaves < n_sub) step(s + kAttnWaves, vb[1], rb[1], vb[0], rb[0]);
-  }
-  } else {
-  // ---- prefill main loop: rounds of kNS sub-tiles per wave (sub-tiles
-  // wave + 4*i), K loaded straight into operand order; a round issues all
-  // of its loads before computing any of them, so one memory latency
-  // covers kNS sub-tiles (the rolling loop above measured slower here:
-  // 955 -> 1,023 us per FP8 prefill step of the 4,096-query chunk)
-  constexpr int kNS = kFp8 ? 2 : 1;  // fp8: 3 measured 990 against 966 us, 4 spills
-  for (int s0 = wave; s0 < n_sub; s0 += kNS * kAttnWaves) {
-    SubTile<kFp8> bt[kNS];
-#pragma unroll
-    for (int i = 0; i < kNS; ++i)
-      if (s0 + i * kAttnWaves < n_sub) load(bt[i], s0 + i * kAttnWaves);
-#pragma unroll
-    for (int i = 0; i < kNS; ++i)
-      if (s0 + i * kAttnWaves < n_sub) compute(bt[i], s0 + i * kAttnWaves);
-  }
   }
 
   // ---- merge the 4 waves.  Each wave publishes its row maxima and sums,
@@ -563,31 +463,24 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
   }
   __syncthreads();
 
-  // ---- write: normalised rows, or (max, sum, accumulator) partials
+  // ---- write the (max, sum, accumulator) partial rows
   for (int e = tid; e < rows_here * kHeadDim; e += kAttnThreads) {
     const int r = e / kHeadDim, d = e % kHeadDim;
     float v = 0.0f;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) v += acc_lds[((size_t)w * 16 + r) * kAccPitch + acc_col(d)];
-    const int rg = row_base + r;
-    if (out_final) {
-      const float Lsum = ml_lds[kAttnWaves * 32 + 16 + r];
-      out_final[(size_t)(rg / gq) * ((size_t)a.Hq * kHeadDim) + (size_t)(rg % gq) * kHeadDim + d] =
-          Lsum > 0.0f ? v * (a.v_scale / Lsum) : 0.0f;
-    } else {
-      out_partial[(size_t)rg * (2 + kHeadDim) + 2 + d] = v;
-    }
+    out_partial[(size_t)(row_base + r) * (2 + kHeadDim) + 2 + d] = v;
   }
-  if (!out_final && tid < rows_here) {
+  if (tid < rows_here) {
     out_partial[(size_t)(row_base + tid) * (2 + kHeadDim)] = ml_lds[kAttnWaves * 32 + tid];
     out_partial[(size_t)(row_base + tid) * (2 + kHeadDim) + 1] = ml_lds[kAttnWaves * 32 + 16 + tid];
   }
 }
 
-// Dynamic LDS: the row statistics, then one region that holds the query
-// tile and the token rows during the main loop and the per-wave
-// accumulators during the merge (the barrier before the merge writes
-// separates the two uses).
+// Dynamic LDS of a decode workgroup: the row statistics, then one region
+// that holds the query tile, the wavefronts' K tiles and the token rows
+// during the main loop and the per-wave accumulators during the merge (the
+// barrier before the merge writes separates the two uses).
 constexpr int kQLdsElems = 16 * (kHeadDim + 16);
 constexpr int kMlFloats = (kAttnWaves + 1) * 32;
 
@@ -628,189 +521,76 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_decode_kernel(AttnArgs a
 
   const uint16_t* q_rows = a.q + ((size_t)b * Q * a.Hq + (size_t)kvh * gq) * kHeadDim;
   float* part = a.partial + (((size_t)b * a.Hkv + kvh) * a.n_splits + split) * n_rows * (2 + kHeadDim);
-  attend_item<kFp8, true>(a, it, kvh, q_rows, a.Hq * kHeadDim, rb * 16, n_rows, gq, acc_lds, ml_lds,
-                          q_lds, k_lds, tok_row, nullptr, part);
-}
-
-template <bool kFp8>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs a) {
-  extern __shared__ float smem[];
-  const int qi = blockIdx.x, kvh = blockIdx.y;
-  const int gq = a.Hq / a.Hkv;
-  float* ml_lds = smem;
-  float* acc_lds = smem + kMlFloats;
-  uint16_t* q_lds = reinterpret_cast<uint16_t*>(acc_lds);
-  int32_t* tok_row = reinterpret_cast<int32_t*>(q_lds + kQLdsElems);
-
-  const int L = a.first_pos + qi + 1;
-  const int G = L / kRatio;
-  ItemDesc it;
-  it.req = a.req;
-  it.sel = a.sel + (size_t)qi * a.K;
-  it.g_begin = 0;
-  it.g_end = min(a.K, G);
-  it.x_begin = kRatio * G;
-  it.x_end = L;
-  it.base_len = L;
-  const uint16_t* q_rows = a.q + ((size_t)qi * a.Hq + (size_t)kvh * gq) * kHeadDim;
-  float* outp = a.out + ((size_t)qi * a.Hq + (size_t)kvh * gq) * kHeadDim;
-  attend_item<kFp8, false>(a, it, kvh, q_rows, 0, 0, gq, gq, acc_lds, ml_lds, q_lds, nullptr,
-                           tok_row, outp, nullptr);
+  attend_item<kFp8>(a, it, kvh, q_rows, a.Hq * kHeadDim, rb * 16, n_rows, gq, acc_lds, ml_lds,
+                    q_lds, k_lds, tok_row, part);
 }
 
 // ---------------------------------------------------------------------------
-// Prefill attention over token partitions.
+// Prefill attention: one wavefront per (query, KV head).
 //
 // The queries of a chunk gather their selected rows from the whole request
 // cache (64 MiB for 32,768 BF16 tokens and two KV heads), far more than one
-// XCD's 4 MiB L2, so a kernel that gives each workgroup one query's whole
-// selection reads most rows from beyond L2.  Here the token axis is cut into
-// ranges of R tokens whose K and V rows for one KV head take about 2 MiB; a
-// partition is (range, KV head).  Workgroups are numbered so that each XCD
-// works through its partitions one after another, each for every query of
-// the chunk, so the current partition's rows stay in that XCD's L2.  A
-// workgroup takes one partition and four consecutive queries, one per
-// wavefront; a wavefront attends over its query's selected tokens inside
-// the range and writes (max, sum, accumulator) rows for the query's heads
-// of that KV head, which combine_ranges_kernel merges over the ranges.
+// XCD's 4 MiB L2.  A wavefront walks its query's selection in ascending
+// token order (the selection is sorted, the current-block tokens come
+// last), so the wavefronts resident on an XCD move through the cache
+// together and the rows they read fall in a sliding window.  Workgroups are
+// numbered so that each XCD serves one KV head (when the number of KV heads
+// divides the 8 XCDs), so that window holds one head's rows.  A workgroup
+// takes four consecutive queries, one per wavefront, and each wavefront
+// writes its query's normalised rows for the heads of its KV head.
+// Measured on the 4,096-query chunk over 32,768 tokens (K = 512), against
+// cutting the token axis into four ranges, one XCD's partition each, with
+// per-range partials merged by a second kernel: BF16 1,200-1,258 ->
+// 1,101-1,113 us per prefill step and 4.8 -> 3.7 GB past L2; FP8, against
+// one workgroup per query, 983-1,006 -> 904-912 us and 3.7 -> 1.0 GB.
 
 constexpr int kXcds = 8;
-constexpr int kRangePitch = kHeadDim + 4;  // partial row: max, sum, 2 unused, accumulator
-// Bytes of K and V rows of one KV head per range (an XCD's L2 holds 4 MiB;
-// measured on the 4,096-query chunk over 32,768 BF16 tokens: 2 MiB ranges
-// 1,824 us per prefill step, 4 MiB 1,648 us, 8 MiB 1,608 us, the per-query
-// kernel 1,950 us).
-#ifndef QSA_RANGE_KIB
-#define QSA_RANGE_KIB 8192
-#endif
-constexpr int kRangeBytes = QSA_RANGE_KIB << 10;
-constexpr int kRangeTok = 1024;            // stream entries translated at a time per wavefront
-constexpr int kRangeGpl = kRangeTok / (kRatio * kWave);  // groups per lane per translation step
-
+constexpr int kPrefillTok = 1024;  // stream entries translated at a time per wavefront
+constexpr int kPrefillGpl = kPrefillTok / (kRatio * kWave);  // groups per lane per step
+// LDS row of one head's output in the write-out: the accumulator at +4 of a
+// 260-float row (the transposed 16-byte stores below then spread over the
+// banks)
+constexpr int kOutPitch = kHeadDim + 4;
 // LDS per wavefront, in floats: the token rows of one translation step,
-// then one sub-tile's K tile; at the end (reused) the transposed partial
+// then one sub-tile's K tile; at the end (reused) the transposed output
 // rows of the query's heads.
-constexpr int kRangeKFloats = k_tile_bytes<false>() / 4;  // room for either element type
-
-constexpr int kRangeWaveFloats = kRangeTok + 16 + kRangeKFloats;
-constexpr int kRangeRowsLds = kRangeWaveFloats / kRangePitch;  // partial rows per LDS pass
-static_assert(kRangeRowsLds >= 8, "a pass holds at least 8 partial rows");
-
-// off[q * (NR + 1) + r] = number of entries of query q's selection (ascending
-// group ids, -1 padded) whose group lies below range r (group < r * R / 4),
-// r = 0 .. NR.  One wavefront per query reads the row in coalesced chunks
-// of 64 entries.  Since the entries ascend, off[r] is the index of the
-// first entry at or past range r: entry e writes the boundaries between the
-// range of entry e - 1 and its own, so every boundary is written once.
-__global__ __launch_bounds__(kAttnThreads) void range_offsets_kernel(
-    const int32_t* __restrict__ sel, int K, int n_q, int R, int NR, int32_t* __restrict__ off) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  const int q = blockIdx.x * kAttnWaves + w;
-  if (q >= n_q) return;
-  const int gpr = R / kRatio;  // groups per range
-  const int32_t* row = sel + (size_t)q * K;
-  int32_t* o = off + (size_t)q * (NR + 1);
-  int prev_r = -1;   // range of the entry before this chunk (wave-uniform)
-  int n_valid = 0;   // valid entries so far (a prefix of the row)
-  for (int c0 = 0; c0 < K; c0 += kWave) {
-    const int e = c0 + lane;
-    const int v = e < K ? row[e] : -1;
-    const int rr = v >= 0 ? min(v / gpr, NR) : -1;
-    int before = __shfl_up(rr, 1, kWave);  // range of entry e - 1
-    if (lane == 0) before = prev_r;
-    if (v >= 0)
-      for (int b = max(before, -1) + 1; b <= rr; ++b) o[b] = e;
-    const uint64_t valid = __ballot(v >= 0);
-    n_valid += __popcll(valid);
-    const int last = valid ? 63 - __clzll(valid) : -1;  // last valid lane of the chunk
-    if (last >= 0) prev_r = __shfl(rr, last, kWave);
-    if (valid != ~0ull) break;  // the valid entries have ended
-  }
-  // boundaries past the last valid entry's range (all of them when the
-  // selection is empty)
-  for (int b = prev_r + 1 + lane; b <= NR; b += kWave) o[b] = n_valid;
-}
-
-// Merge of the prefill range partials, one workgroup per (query, KV head):
-// out = sum_r 2^(m_r - M) acc_r / sum_r 2^(m_r - M) l_r over the ranges r.
-// The first gq threads turn each head's (max, sum) pairs into one factor
-// per partial row; then every thread owns four output dimensions of one
-// head at a time, with all of that head's range loads in flight together.
-constexpr int kMaxRanges = 32;
-__global__ __launch_bounds__(kHeadDim) void combine_ranges_kernel(
-    const float* __restrict__ part, int NR, int Hq, int Hkv, float v_scale,
-    float* __restrict__ out) {
-  __shared__ float fac[kMaxRanges * 16];
-  const int b = blockIdx.x / Hkv, kvh = blockIdx.x - b * Hkv;
-  const int gq = Hq / Hkv, t = threadIdx.x;
-  const float* p = part + ((size_t)b * Hkv + kvh) * NR * gq * kRangePitch;
-  if (t < gq) {
-    float M = -INFINITY;
-    for (int s = 0; s < NR; ++s) M = fmaxf(M, p[((size_t)s * gq + t) * kRangePitch]);
-    float den = 0.0f;
-    for (int s = 0; s < NR; ++s) {
-      const float* row = p + ((size_t)s * gq + t) * kRangePitch;
-      const float f = row[0] == -INFINITY ? 0.0f : exp2f(row[0] - M);
-      fac[s * gq + t] = f;
-      den += f * row[1];
-    }
-    // a head with no visible token (den = 0) outputs exact zeros
-    const float sc = den > 0.0f ? v_scale / den : 0.0f;
-    for (int s = 0; s < NR; ++s) fac[s * gq + t] *= sc;
-  }
-  __syncthreads();
-  constexpr int kRowsPerPass = kHeadDim / (kHeadDim / 4);  // 4 heads per pass
-  const int d4 = t % (kHeadDim / 4), r0 = t / (kHeadDim / 4);
-  for (int r = r0; r < gq; r += kRowsPerPass) {
-    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-    for (int s = 0; s < NR; ++s) {
-      const float4 v = *reinterpret_cast<const float4*>(p + ((size_t)s * gq + r) * kRangePitch +
-                                                        4 + 4 * d4);
-      const float f = fac[s * gq + r];
-      num.x += f * v.x; num.y += f * v.y; num.z += f * v.z; num.w += f * v.w;
-    }
-    *reinterpret_cast<float4*>(out + ((size_t)b * Hq + (size_t)kvh * gq + r) * kHeadDim +
-                               4 * d4) = num;
-  }
-}
+constexpr int kPrefillKFloats = k_tile_bytes<false>() / 4;  // room for either element type
+constexpr int kPrefillWaveFloats = kPrefillTok + 16 + kPrefillKFloats;
+constexpr int kOutRowsLds = kPrefillWaveFloats / kOutPitch;  // output rows per LDS pass
+static_assert(kOutRowsLds >= 8, "a pass holds at least 8 output rows");
 
 template <bool kFp8>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_ranges_kernel(
-    AttnArgs a, int R, int NR, int n_qb, const int32_t* __restrict__ off,
-    float* __restrict__ part) {
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs a, int n_qb) {
   extern __shared__ float smem[];
   const int gq = a.Hq / a.Hkv;
-  // workgroup -> (partition p, query block qb): XCD x (= blockIdx % 8, the
-  // order in which workgroups are dealt to the XCDs) takes partitions
-  // x, x + 8, ... in turn, every query block of one before the next
+  // workgroup -> (KV head, query block qb).  With nx = 8 / Hkv, XCD x (=
+  // blockIdx % 8, the order in which workgroups are dealt to the XCDs)
+  // serves KV head x / nx; other head counts take the linear order.
   const int b = blockIdx.x;
-  const int xcd = b % kXcds, i = b / kXcds;
-  const int j = i / n_qb, qb = i - j * n_qb;
-  const int p = kXcds * j + xcd;
-  if (p >= NR * a.Hkv) return;  // padding partition: the whole workgroup leaves
-  const int r = p / a.Hkv, kvh = p - r * a.Hkv;
+  int kvh, qb;
+  if (kXcds % a.Hkv == 0) {
+    const int nx = kXcds / a.Hkv, xcd = b % kXcds;
+    kvh = xcd / nx;
+    qb = (b / kXcds) * nx + xcd % nx;
+  } else {
+    kvh = b % a.Hkv;
+    qb = b / a.Hkv;
+  }
+  if (qb >= n_qb) return;  // padding: the whole workgroup leaves
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int lq = lane & 15, lg = lane >> 4;
   const int q = qb * kAttnWaves + wave;
   if (q >= a.batch) return;  // whole wavefronts; nothing below synchronises the block
-  float* wl = smem + (size_t)wave * kRangeWaveFloats;
+  float* wl = smem + (size_t)wave * kPrefillWaveFloats;
   int32_t* tok = reinterpret_cast<int32_t*>(wl);
-  uint8_t* k_lds = reinterpret_cast<uint8_t*>(wl + kRangeTok + 16);
+  uint8_t* k_lds = reinterpret_cast<uint8_t*>(wl + kPrefillTok + 16);
 
-  // the query's selected groups and current-block tokens inside the range
+  // the query's selected groups (all complete, all visible), then its
+  // current-block tokens 4G .. L - 1
   const int L = a.first_pos + q + 1;
   const int G = L / kRatio;
-  const int n_valid = min(a.K, G);
-  const int t0 = r * R, t1 = min(t0 + R, L);
-  int lo = 0, hi = 0, x0 = 0, x1 = 0;
-  if (t0 < L) {
-    lo = min(off[(size_t)q * (NR + 1) + r], n_valid);
-    hi = min(off[(size_t)q * (NR + 1) + r + 1], n_valid);
-    x0 = max(kRatio * G, t0);
-    x1 = max(x0, t1);
-  }
-  const int n_groups = max(0, hi - lo), n_extra = x1 - x0;
+  const int n_groups = min(a.K, G);
+  const int x0 = kRatio * G, n_extra = L - x0;
   const int n_stream = kRatio * n_groups + n_extra;
 
   // the query rows as the Q^T operand, held in registers: row lq (head
@@ -833,24 +613,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_ranges_kernel(
   const uint8_t* kc = reinterpret_cast<const uint8_t*>(a.k);
   const uint8_t* vc = reinterpret_cast<const uint8_t*>(a.v);
   const int32_t* pt = a.page_table + (size_t)a.req * a.max_pages;
-  const int32_t* srow = a.sel + (size_t)q * a.K + lo;
+  const int32_t* srow = a.sel + (size_t)q * a.K;
 
-  for (int c0 = 0; c0 < n_stream; c0 += kRangeTok) {
+  for (int c0 = 0; c0 < n_stream; c0 += kPrefillTok) {
     // stream entries c0 + 4*(u*64 + lane) .. + 3 -> physical rows: a selected
     // group's four tokens (one page), or up to four current-block tokens.
     // All of a lane's selection loads are issued before its page-table
     // loads, so a step costs two memory round trips.
     {
-      int gs[kRangeGpl], ph[kRangeGpl];
+      int gs[kPrefillGpl], ph[kPrefillGpl];
 #pragma unroll
-      for (int u = 0; u < kRangeGpl; ++u) {
+      for (int u = 0; u < kPrefillGpl; ++u) {
         const int e = c0 + kRatio * (u * kWave + lane);
         gs[u] = e < kRatio * n_groups ? srow[e / kRatio] : -1;
       }
 #pragma unroll
-      for (int u = 0; u < kRangeGpl; ++u) ph[u] = gs[u] >= 0 ? pt[(kRatio * gs[u]) / kPage] : -1;
+      for (int u = 0; u < kPrefillGpl; ++u) ph[u] = gs[u] >= 0 ? pt[(kRatio * gs[u]) / kPage] : -1;
 #pragma unroll
-      for (int u = 0; u < kRangeGpl; ++u) {
+      for (int u = 0; u < kPrefillGpl; ++u) {
         const int e = c0 + kRatio * (u * kWave + lane);
         int4 rr = make_int4(-1, -1, -1, -1);
         if (e < kRatio * n_groups) {
@@ -880,7 +660,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_ranges_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int n_sub = min(kRangeTok / 16, (n_stream - c0 + 15) / 16);
+    const int n_sub = min(kPrefillTok / 16, (n_stream - c0 + 15) / 16);
     // K rows one sub-tile ahead: sub-tile s + 1's loads are issued into the
     // registers s's rows leave once they are in LDS, so they arrive while s
     // computes
@@ -914,21 +694,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_ranges_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // ---- the partial rows: row lq's sum over its four lanes, then the
+  // ---- the query's rows: row lq's sum over its four lanes, the normalised
   // accumulator transposed through LDS (acc[mb][i] of lane (lq, lg) is
   // dimension out_dim(lg, i, mb); runs of four consecutive mb are four
   // consecutive dimensions) and written with 16-byte stores, up to
-  // kRangeRowsLds rows at a time
+  // kOutRowsLds rows at a time
   float l = l_run;
   l += __shfl_xor(l, 16, kWave);
   l += __shfl_xor(l, 32, kWave);
-  float4* dst = reinterpret_cast<float4*>(part + (((size_t)q * a.Hkv + kvh) * NR + r) * gq *
-                                                     kRangePitch);
+  const float f = l > 0.0f ? a.v_scale / l : 0.0f;  // no visible token: zeros
+#pragma unroll
+  for (int mb = 0; mb < 16; ++mb)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[mb][k] *= f;
+  float4* dst = reinterpret_cast<float4*>(a.out + ((size_t)q * a.Hq + (size_t)kvh * gq) * kHeadDim);
   const float4* srcl = reinterpret_cast<const float4*>(wl);
-  for (int h0 = 0; h0 < gq; h0 += kRangeRowsLds) {
-    if (lq >= h0 && lq < min(gq, h0 + kRangeRowsLds)) {
-      float* rowp = wl + (lq - h0) * kRangePitch;
-      if (lg == 0) *reinterpret_cast<float4*>(rowp) = make_float4(m_run, l, 0.0f, 0.0f);
+  for (int h0 = 0; h0 < gq; h0 += kOutRowsLds) {
+    if (lq >= h0 && lq < min(gq, h0 + kOutRowsLds)) {
+      float* rowp = wl + (lq - h0) * kOutPitch;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -939,8 +722,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_ranges_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int nf4 = (min(gq, h0 + kRangeRowsLds) - h0) * (kRangePitch / 4);
-    for (int e = lane; e < nf4; e += kWave) dst[h0 * (kRangePitch / 4) + e] = srcl[e];
+    const int nf4 = (min(gq, h0 + kOutRowsLds) - h0) * (kHeadDim / 4);
+    for (int e = lane; e < nf4; e += kWave) {
+      const int rw = e / (kHeadDim / 4), c = e % (kHeadDim / 4);
+      dst[(h0 + rw) * (kHeadDim / 4) + c] = srcl[rw * (kOutPitch / 4) + 1 + c];
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1015,10 +801,10 @@ __global__ void expand_tokens_kernel(const int32_t* __restrict__ sel, int K,
   }
 }
 
-size_t attn_smem_bytes(int stream_cap, bool k_tiles) {
+size_t attn_smem_bytes(int stream_cap) {
   const size_t acc = sizeof(float) * (size_t)kAttnWaves * 16 * kAccPitch;
   const size_t loop = sizeof(uint16_t) * (size_t)kQLdsElems +
-                      (k_tiles ? (size_t)kAttnWaves * kItemKBytesPerWave : 0) +
+                      (size_t)kAttnWaves * kItemKBytesPerWave +
                       sizeof(int32_t) * (size_t)((stream_cap + 15) / 16 * 16);
   return sizeof(float) * (size_t)kMlFloats + (acc > loop ? acc : loop);
 }
@@ -1027,7 +813,7 @@ template <bool kFp8>
 hipError_t launch_decode_t(const AttnArgs& a, hipStream_t stream) {
   if (a.n_splits > kMaxSplits) return hipErrorInvalidValue;
   const int cap = 4 * a.groups_per_split + 3 + (a.q_per_req - 1);
-  const size_t smem = attn_smem_bytes(cap, true);
+  const size_t smem = attn_smem_bytes(cap);
   const int rows = a.q_per_req * (a.Hq / a.Hkv);
   const int nblk = (rows + 15) / 16;
   dim3 grid(a.n_splits * nblk * a.Hkv * a.batch);
@@ -1040,40 +826,18 @@ hipError_t launch_decode_t(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// FP8 K/V: one workgroup per (query, KV head) over the query's whole
-// selection.  Its rows are half the size of BF16 rows, and the per-query
-// kernel already finds over half of them in L2 (measured: 1,010 us per
-// prefill step of the 4,096-query chunk against 1,143 us with ranges).
-hipError_t launch_prefill_per_query(const AttnArgs& a, hipStream_t stream) {
-  if (a.Hq / a.Hkv > 16) return hipErrorInvalidValue;
-  const size_t smem = attn_smem_bytes(4 * a.K + 3, false);
-  dim3 grid(a.batch, a.Hkv);
-  hipLaunchKernelGGL((attn_prefill_kernel<true>), grid, dim3(kAttnThreads), smem, stream, a);
-  return hipGetLastError();
-}
-
-// Range partitions (attn_prefill_ranges_kernel), then the merge; taken for
-// BF16 K/V (FP8 measured slower here than the per-query kernel: 1,055 against
-// 983 us per prefill step of the 4,096-query chunk).
 template <bool kFp8>
-hipError_t launch_prefill_ranges(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
   if (a.Hq / a.Hkv > 16) return hipErrorInvalidValue;
-  if (!a.range_offsets || !a.partial) return hipErrorInvalidValue;
-  int R, NR;
-  prefill_ranges(a.kv_dtype, a.Hkv, a.max_ctx, &R, &NR);
   const int n_qb = (a.batch + kAttnWaves - 1) / kAttnWaves;
-  hipLaunchKernelGGL(range_offsets_kernel, dim3(n_qb), dim3(kAttnThreads), 0, stream, a.sel, a.K,
-                     a.batch, R, NR, a.range_offsets);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int np_pad = (NR * a.Hkv + kXcds - 1) / kXcds * kXcds;
-  const size_t smem = sizeof(float) * (size_t)kAttnWaves * kRangeWaveFloats;
-  hipLaunchKernelGGL((attn_prefill_ranges_kernel<kFp8>), dim3((unsigned)((size_t)n_qb * np_pad)),
-                     dim3(kAttnThreads), smem, stream, a, R, NR, n_qb, a.range_offsets, a.partial);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_ranges_kernel, dim3((unsigned)((size_t)a.batch * a.Hkv)),
-                     dim3(kHeadDim), 0, stream, a.partial, NR, a.Hq, a.Hkv, a.v_scale, a.out);
+  size_t n_wg = (size_t)n_qb * a.Hkv;
+  if (kXcds % a.Hkv == 0) {
+    const int nx = kXcds / a.Hkv;
+    n_wg = (size_t)((n_qb + nx - 1) / nx) * kXcds;
+  }
+  const size_t smem = sizeof(float) * (size_t)kAttnWaves * kPrefillWaveFloats;
+  hipLaunchKernelGGL((attn_prefill_kernel<kFp8>), dim3((unsigned)n_wg), dim3(kAttnThreads), smem,
+                     stream, a, n_qb);
   return hipGetLastError();
 }
 
@@ -1082,39 +846,11 @@ hipError_t launch_prefill_ranges(const AttnArgs& a, hipStream_t stream) {
 // then mostly come from the caches.
 hipError_t dispatch(const AttnArgs& a, hipStream_t stream, bool prefill) {
   if (a.kv_dtype == 1)
-    return prefill ? launch_prefill_per_query(a, stream) : launch_decode_t<true>(a, stream);
-  return prefill ? launch_prefill_ranges<false>(a, stream) : launch_decode_t<false>(a, stream);
+    return prefill ? launch_prefill_t<true>(a, stream) : launch_decode_t<true>(a, stream);
+  return prefill ? launch_prefill_t<false>(a, stream) : launch_decode_t<false>(a, stream);
 }
 
 }  // namespace
-
-void prefill_ranges(int kv_dtype, int Hkv, int max_ctx, int* R, int* NR) {
-  // K + V rows of one KV head for R tokens take kRangeBytes; at least 8
-  // partitions so every XCD has one; at most 32 ranges
-  const int esize = kv_dtype == 1 ? 1 : 2;
-  const int r_l2 = kRangeBytes / (2 * kHeadDim * esize);
-  const int ctx = max(max_ctx, 1);
-  int nr = (ctx + r_l2 - 1) / r_l2;
-  nr = max(nr, (kXcds + Hkv - 1) / Hkv);
-  nr = min(nr, kMaxRanges);
-  int r = (ctx + nr - 1) / nr;
-  r = (r + kPage - 1) / kPage * kPage;
-  *R = r;
-  *NR = (ctx + r - 1) / r;
-}
-
-size_t prefill_attn_workspace_bytes(int kv_dtype, int Hq, int Hkv, int n_q, int max_ctx,
-                                    size_t* off_bytes) {
-  if (kv_dtype == 1) {  // the per-query kernel needs no workspace
-    if (off_bytes) *off_bytes = 0;
-    return 0;
-  }
-  int R, NR;
-  prefill_ranges(kv_dtype, Hkv, max_ctx, &R, &NR);
-  const size_t ob = ((size_t)n_q * (NR + 1) * sizeof(int32_t) + 255) / 256 * 256;
-  if (off_bytes) *off_bytes = ob;
-  return ob + sizeof(float) * (size_t)n_q * Hkv * NR * (Hq / Hkv) * kRangePitch;
-}
 
 hipError_t launch_sparse_attn_decode(const AttnArgs& a, hipStream_t stream) {
   if (a.batch <= 0) return hipSuccess;

@@ -1,6 +1,6 @@
 /* Host-side memory and undefined-behaviour check of libqsa's C ABI: the
  * geometry validation, token widths, workspace sizes (including the
- * prefill range partitions and the decode split layout) and every entry
+ * decode split layout) and every entry
  * point's argument checks, run in a build whose host code carries
  * AddressSanitizer and UndefinedBehaviorSanitizer.  Every call here is
  * decided on the host before any HIP call, so no GPU is needed; any report

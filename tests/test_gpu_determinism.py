@@ -30,7 +30,8 @@ def test_decode_repeats_bitwise(gpu):
 
 @pytest.mark.parametrize("kv", ["fp8", "bf16"])
 def test_prefill_repeats_bitwise(gpu, kv):
-    # fp8: the per-query kernel; bf16: range partitions and their merge
+    # both element types: scoring, top-K, and attention with one wavefront
+    # per (query, KV head)
     import torch
     wl = workload.prefill_workload(950, 3000, 300, kv_dtype=kv, topk_groups=256)
     d = H.to_dev(wl, gpu)
@@ -92,9 +93,9 @@ def test_decode_graph_replay_matches_eager(gpu):
 
 
 def test_prefill_graph_replay_matches_eager(gpu):
-    # a BF16 prefill step (scoring, top-K, range offsets, range partitions,
-    # merge) captured in a HIP graph replays to the eager result, with the
-    # query rows changed and eager prefill calls between the replays
+    # a BF16 prefill step (scoring, top-K, attention) captured in a HIP
+    # graph replays to the eager result, with the query rows changed and
+    # eager prefill calls between the replays
     import torch
     import learned_sparse_attention_amd as qsa
     wl = workload.prefill_workload(952, 5000, 300, kv_dtype="bf16", topk_groups=256)

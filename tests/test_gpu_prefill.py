@@ -208,8 +208,8 @@ def test_prefill_rows_of_every_length_past_16384_groups(gpu):
 @pytest.mark.parametrize("n_q,kv", [(1, "fp8"), (257, "bf16")])
 def test_prefill_head_shapes(gpu, hq, hkv, n_q, kv):
     # the operator suite's local head shapes at 1 and 257 query rows, and
-    # the widest group (16 query heads per KV head: the range kernel's
-    # partial rows then take two LDS passes)
+    # the widest group (16 query heads per KV head: the output rows then
+    # take two LDS passes); one KV head spreads its queries over all 8 XCDs
     wl = workload.prefill_workload(840 + 7 * hq + hkv + n_q, 2500, n_q, num_q_heads=hq,
                                    num_kv_heads=hkv, kv_dtype=kv, topk_groups=512)
     _prefill_check(wl, gpu, np.arange(n_q))
@@ -225,29 +225,38 @@ def test_prefill_topk_paths_and_budgets(gpu, first_pos, n_q, K, kv):
     _prefill_check(wl, gpu, _sample_rows(wl.n_q, 6))
 
 
-# BF16 prefill attention works on token-range partitions (ranges whose K
-# and V rows for one KV head take 8 MiB, at most 32 ranges); the cases
-# below stress the per-range bookkeeping: few selected groups per range,
-# the 32-range cap at full capacity, and selections piled into one range.
+@pytest.mark.parametrize("hq,hkv,kv", [(24, 3, "bf16"), (16, 4, "fp8"), (16, 8, "bf16"),
+                                        (32, 16, "fp8")])
+def test_prefill_kv_head_counts(gpu, hq, hkv, kv):
+    # KV head counts that divide the 8 XCDs (4, 8: each XCD serves one head)
+    # and that do not (3, 16: workgroups in plain (query block, head) order)
+    wl = workload.prefill_workload(880 + hq + hkv, 2500, 257, num_q_heads=hq, num_kv_heads=hkv,
+                                   kv_dtype=kv, topk_groups=512)
+    _prefill_check(wl, gpu, np.arange(wl.n_q))
+
+
+# Prefill attention walks each query's whole selection in token order, one
+# wavefront per (query, KV head); the cases below stress the token stream:
+# few selected groups, the longest selections at full capacity, and
+# selections piled into one 8,192-token region that every query reads.
 
 @pytest.mark.parametrize("K", [1, 7, 100])
-def test_prefill_ranges_small_budgets(gpu, K):
+def test_prefill_small_budgets(gpu, K):
     wl = workload.prefill_workload(860 + K, 20000, 300, kv_dtype="bf16", topk_groups=K)
     _prefill_check(wl, gpu, np.arange(wl.n_q))
 
 
-def test_prefill_ranges_at_full_capacity(gpu):
-    # 64 queries ending a 262,144-token request: 32 ranges of 8,192 tokens
+def test_prefill_at_full_capacity(gpu):
+    # 64 queries ending a 262,144-token request, 2,048 groups each
     wl = workload.prefill_workload(863, 262144 - 64, 64, kv_dtype="bf16", topk_groups=2048)
     assert wl.first_pos + wl.n_q == 262144
     _prefill_check(wl, gpu, np.arange(wl.n_q))
 
 
-def test_prefill_ranges_selection_in_one_range(gpu):
+def test_prefill_selection_in_one_region(gpu):
     # every query shares one indexer query, and the groups of tokens
-    # 16,384 .. 24,575 (one 8,192-token range) score far above the rest:
-    # each selection lies wholly in that range, the others hold only the
-    # current block
+    # 16,384 .. 24,575 score far above the rest: each selection lies wholly
+    # in that region, then comes the query's current block
     wl = workload.prefill_workload(864, 30000, 96, kv_dtype="bf16", topk_groups=512)
     wl.q_idx[:] = wl.q_idx[0]
     wl.w_idx[:] = wl.w_idx[0]
