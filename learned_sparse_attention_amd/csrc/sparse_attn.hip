@@ -167,19 +167,11 @@ __device__ __forceinline__ void store_k_tile(const u32x4 (&k)[kFp8 ? 4 : 8], uin
     *reinterpret_cast<u32x4*>(tile + t * kRowBytes + 16 * ((4 * j + c) ^ sw)) = k[j];
 }
 
-// The K operand of k-step ks (token lq, dims qk_dim(ks, lg) + 0..7, as
-// bf16) from the LDS tile; sw = k_swizzle(lq).
-template <bool kFp8>
-__device__ __forceinline__ bf16x8 k_operand_lds(const uint8_t* tile, int ks, int lq, int lg,
-                                                int sw) {
-  constexpr int kRowBytes = kHeadDim * (kFp8 ? 1 : 2);
-  if (kFp8) {
-    // chunk 4 (ks / 2) + lg holds dims 64 (ks / 2) + 16 lg .. + 15
-    const u32x4 w =
-        *reinterpret_cast<const u32x4*>(tile + lq * kRowBytes + 16 * ((4 * (ks >> 1) + lg) ^ sw));
-    return (ks & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
-  }
-  return *reinterpret_cast<const bf16x8*>(tile + lq * kRowBytes + 16 * ((4 * ks + lg) ^ sw));
+// The BF16 K operand of k-step ks (token lq, dims qk_dim(ks, lg) + 0..7)
+// from the LDS tile; sw = k_swizzle(lq).
+__device__ __forceinline__ bf16x8 k_operand_lds_bf16(const uint8_t* tile, int ks, int lq, int lg,
+                                                     int sw) {
+  return *reinterpret_cast<const bf16x8*>(tile + lq * (2 * kHeadDim) + 16 * ((4 * ks + lg) ^ sw));
 }
 
 // LDS of one wavefront's K tile (room for either element type)
@@ -196,6 +188,31 @@ __device__ __forceinline__ float4_t subtile_logits(KOp kop, QOp qop) {
     sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop(ks), __builtin_bit_cast(bf16x8, qop(ks)), sc,
                                                 0, 0, 0);
   return sc;
+}
+
+// S^T = K . Q^T of one sub-tile with K from the LDS tile (sw =
+// k_swizzle(lq)) and the Q^T operand qop(ks).  For FP8 the four 16-byte
+// chunks of the lane's row are read whole before the products: each serves
+// two k-steps, and reading each k-step's half on its own (two dwords, which
+// the compiler does when one half is used at a time) costs those reads
+// two-way bank conflicts.
+template <bool kFp8, typename QOp>
+__device__ __forceinline__ float4_t subtile_logits_lds(const uint8_t* tile, int lq, int lg, int sw,
+                                                       QOp qop) {
+  if constexpr (kFp8) {
+    u32x4 c[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      c[m] = *reinterpret_cast<const u32x4*>(tile + lq * kHeadDim + 16 * ((4 * m + lg) ^ sw));
+    return subtile_logits(
+        [&](int ks) {
+          const u32x4 w = c[ks >> 1];
+          return (ks & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
+        },
+        qop);
+  } else {
+    return subtile_logits([&](int ks) { return k_operand_lds_bf16(tile, ks, lq, lg, sw); }, qop);
+  }
 }
 
 // The online-softmax update of one sub-tile from its logits sc: the
@@ -405,8 +422,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
       vis[i] = rcur[i] >= 0 && tok < limit;
     }
     const float4_t sc =
-        subtile_logits([&](int ks) { return k_operand_lds<kFp8>(tile, ks, lq, lg, kr_swz); },
-                       [&](int ks) { return qop[ks]; });
+        subtile_logits_lds<kFp8>(tile, lq, lg, kr_swz, [&](int ks) { return qop[ks]; });
     subtile_accumulate<kFp8>(sc, vcur, rcur, vis, qk_scale, m_run, l_run, acc);
     // the next store to the tile comes after these operand reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -681,8 +697,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs 
 #pragma unroll
       for (int k = 0; k < 4; ++k) vis[k] = rv[k] >= 0;
       const float4_t sc =
-          subtile_logits([&](int ks) { return k_operand_lds<kFp8>(k_lds, ks, lq, lg, kr_swz); },
-                         [&](int ks) { return qop[ks]; });
+          subtile_logits_lds<kFp8>(k_lds, lq, lg, kr_swz, [&](int ks) { return qop[ks]; });
       subtile_accumulate<kFp8>(sc, vr, rv, vis, qk_scale, m_run, l_run, acc);
       // the next sub-tile's stores come after these operand reads
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
