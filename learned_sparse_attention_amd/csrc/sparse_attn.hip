@@ -75,8 +75,9 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 // so the contraction index of S^T = K . Q^T is permuted identically in both
 // operands; in k-step ks, lane group lg supplies
 //   bf16 K: d = 32*ks + 8*lg + 0..7,
-//   fp8 K:  d = 64*(ks/2) + 16*lg + 8*(ks%2) + 0..7 (one 16-byte load
-//           serves two k-steps).
+//   fp8 K:  d = 64*(ks/2) + 16*lg + 8*(ks%2) + 0..7 (one 16-byte chunk of
+//           the row serves two k-steps),
+// so each K operand is one 16-byte chunk of the token's row in LDS.
 // The output dimension of O^T = V^T . P^T is permuted through the V^T
 // operand: lane lq of m-block mb supplies d = dv(lq, mb) with
 //   bf16 V: dv = 8*lq + (mb % 8) + 128*(mb / 8) (two loads of 256
@@ -84,6 +85,7 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 //   fp8 V:  dv = 16*lq + mb (one load of the whole 256-byte row);
 // so accumulator acc[mb][i] of lane (lq, lg) holds output dimension
 // dv(4*lg + i, mb) of query row lq (out_dim below).
+
 // First of the 8 dimensions that k-step ks of lane group lg covers.
 template <bool kFp8>
 __device__ __forceinline__ int qk_dim(int ks, int lg) {
@@ -118,13 +120,13 @@ __device__ __forceinline__ void load_v_rows(u32x4 (&v)[4][kFp8 ? 1 : 2], int (&r
   }
 }
 
-// K rows through LDS.  Read straight into
-// MFMA operand order, the 64 lanes of one load instruction touch 16
+// K rows through LDS.  Read straight into MFMA operand order, the 64
+// lanes of one load instruction would touch 16
 // different rows with adjacent lanes in different rows, so no four lanes
-// share a 64-byte segment and the vector L1 serves 64 separate accesses per
-// instruction, four times the 16 of a load whose lane quads read contiguous
-// 64 bytes; where the gathers run at L1 rate, that access count bounds
-// them.  Instead lane 4t + c reads bytes 64j + 16c of token t's row in load
+// would share a 64-byte segment and the vector L1 would serve 64 separate
+// accesses per instruction, four times the 16 of a load whose lane quads
+// read contiguous 64 bytes; where the gathers run at L1 rate, that access
+// count bounds them.  Instead lane 4t + c reads bytes 64j + 16c of token t's row in load
 // j (contiguous quads), stores them to a per-wavefront LDS tile, and the
 // operands are read back per k-step.  The 16-byte chunk k of token t's row
 // sits at chunk position k ^ k_swizzle(t) of LDS row t.  This XOR pattern
@@ -326,8 +328,8 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
   // Selected groups: a group's 4 tokens share one page (4 divides the page
   // size), so each thread takes whole groups, kGroupBatch at a time, with
   // all their selection loads issued before any page-table load: a long
-  // (prefill) selection then costs two memory round trips per batch, not
-  // two per token.
+  // selection then costs two memory round trips per batch, not two per
+  // token.
   constexpr int kGroupBatch = 4;
   for (int j0 = 0; j0 < n_groups; j0 += kGroupBatch * kAttnThreads) {
     int gs[kGroupBatch], ph[kGroupBatch];
@@ -551,14 +553,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_decode_kernel(AttnArgs a
 // last), so the wavefronts resident on an XCD move through the cache
 // together and the rows they read fall in a sliding window.  Workgroups are
 // numbered so that each XCD serves one KV head (when the number of KV heads
-// divides the 8 XCDs), so that window holds one head's rows.  A workgroup
-// takes four consecutive queries, one per wavefront, and each wavefront
-// writes its query's normalised rows for the heads of its KV head.
-// Measured on the 4,096-query chunk over 32,768 tokens (K = 512), against
-// cutting the token axis into four ranges, one XCD's partition each, with
-// per-range partials merged by a second kernel: BF16 1,200-1,258 ->
-// 1,101-1,113 us per prefill step and 4.8 -> 3.7 GB past L2; FP8, against
-// one workgroup per query, 983-1,006 -> 904-912 us and 3.7 -> 1.0 GB.
+// divides the 8 XCDs), so that window holds one head's rows (worth about
+// 1 % against the plain order).  A workgroup takes four consecutive queries,
+// one per wavefront, and each wavefront writes its query's normalised rows
+// for the heads of its KV head.  Measured on the 4,096-query chunk over
+// 32,768 tokens (K = 512), against cutting the token axis into four ranges,
+// one XCD's partition each, with per-range partials merged by a second
+// kernel: BF16 1,204-1,241 -> 1,085-1,108 us per prefill step and 4.8 ->
+// 3.7-4.4 GB past L2; FP8, against one workgroup per query, 963-973 ->
+// 883-889 us and 3.7 -> 1.1 GB.
 
 constexpr int kXcds = 8;
 constexpr int kPrefillTok = 1024;  // stream entries translated at a time per wavefront
