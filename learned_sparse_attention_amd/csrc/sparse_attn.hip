@@ -256,19 +256,31 @@ __device__ __forceinline__ void subtile_accumulate(float4_t sc, u32x4 (&v)[4][kF
     for (int mb = 0; mb < 16; ++mb) acc[mb] *= alpha;
     m_run = m_new;
   }
-  // weights as a bf16 hi + lo pair (~16 significant bits) for the PV MFMA
+  // The weights for the P.V MFMA.  BF16 K/V: a bf16 hi + lo pair (~16
+  // significant bits), which keeps the output within ~1e-6 of exact.  FP8
+  // K/V: one bf16 value per weight (V itself carries 3 mantissa bits), and
+  // the sum l takes the rounded weights, so the output is exactly the
+  // average of V under those weights: max-abs error ~4e-4 against 2e-2
+  // allowed, 16 fewer MFMAs per sub-tile (measured: FP8 prefill attention
+  // 796-814 -> 692-701 us, decode 195.85 -> 195.05 us per step; with BF16
+  // K/V the single form measured slower, 951 -> 1,108-1,139 us).
   float psum = 0.0f;
   uint32_t hb[4], lb[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float pw = (m_run == -INFINITY) ? 0.0f : exp2f(sv[i] - m_run);
     hb[i] = bf16_rne_bits(pw);
-    lb[i] = bf16_rne_bits(pw - __uint_as_float(hb[i] << 16));
-    psum += pw;
+    if (kFp8) {
+      psum += __uint_as_float(hb[i] << 16);
+    } else {
+      lb[i] = bf16_rne_bits(pw - __uint_as_float(hb[i] << 16));
+      psum += pw;
+    }
   }
   l_run += psum;
   const short4_t p_hi = (short4_t){(short)hb[0], (short)hb[1], (short)hb[2], (short)hb[3]};
-  const short4_t p_lo = (short4_t){(short)lb[0], (short)lb[1], (short)lb[2], (short)lb[3]};
+  short4_t p_lo = {};
+  if (!kFp8) p_lo = (short4_t){(short)lb[0], (short)lb[1], (short)lb[2], (short)lb[3]};
   // O^T += V^T . P^T; m-block mb holds d = out_dim(lg', i, mb) for D row 4*lg' + i
 #pragma unroll
   for (int qd = 0; qd < 8; ++qd) {
@@ -293,7 +305,7 @@ __device__ __forceinline__ void subtile_accumulate(float4_t sc, u32x4 (&v)[4][kF
       const uint32_t hi = __builtin_amdgcn_perm(cv[3], cv[2], sel);
       const short4_t vop = __builtin_bit_cast(short4_t, (u32x2){lo, hi});
       acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, p_hi, acc[mb], 0, 0, 0);
-      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, p_lo, acc[mb], 0, 0, 0);
+      if (!kFp8) acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, p_lo, acc[mb], 0, 0, 0);
     }
   }
 }
@@ -354,7 +366,9 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
     }
   }
   // the contiguous extra tokens, then padding to whole sub-tiles
-  for (int i = kRatio * n_groups + tid; i < n_sub * 16; i += kAttnThreads) {
+  // (one sub-tile per wavefront more: the main loop's prefetch past the
+  // last sub-tile reads those absent entries, i.e. row 0)
+  for (int i = kRatio * n_groups + tid; i < (n_sub + kAttnWaves) * 16; i += kAttnThreads) {
     int r = -1;
     if (i < n_stream) {
       const int t = it.x_begin + (i - kRatio * n_groups);
@@ -404,11 +418,12 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const ItemDesc& i
   auto step = [&](int s, u32x4 (&vcur)[4][kFp8 ? 1 : 2], int (&rcur)[4],
                   u32x4 (&vnext)[4][kFp8 ? 1 : 2], int (&rnext)[4]) {
     store_k_tile<kFp8>(kst, tile);
+    // unconditional (past the last sub-tile it reads absent entries): under
+    // a branch, the compiler's wait before the P.V products covered this
+    // prefetch too (vmcnt(0) instead of a count that leaves it in flight)
     const int sn = s + kAttnWaves;
-    if (sn < n_sub) {
-      load_k_quads<kFp8>(kst, tok_row + 16 * sn, kc, Hkv, kvh);
-      load_v_rows<kFp8, true>(vnext, rnext, tok_row + 16 * sn, vc, Hkv, kvh);
-    }
+    load_k_quads<kFp8>(kst, tok_row + 16 * sn, kc, Hkv, kvh);
+    load_v_rows<kFp8, true>(vnext, rnext, tok_row + 16 * sn, vc, Hkv, kvh);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -603,6 +618,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs 
   float* wl = smem + (size_t)wave * kPrefillWaveFloats;
   int32_t* tok = reinterpret_cast<int32_t*>(wl);
   uint8_t* k_lds = reinterpret_cast<uint8_t*>(wl + kPrefillTok + 16);
+  // the 16 entries past a translation step: absent, so the K prefetch past
+  // a step's last sub-tile reads row 0 (the translation writes the rest)
+  if (lane < 16) tok[kPrefillTok + lane] = -1;
 
   // the query's selected groups (all complete, all visible), then its
   // current-block tokens 4G .. L - 1
@@ -682,7 +700,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs 
     const int n_sub = min(kPrefillTok / 16, (n_stream - c0 + 15) / 16);
     // K rows one sub-tile ahead: sub-tile s + 1's loads are issued into the
     // registers s's rows leave once they are in LDS, so they arrive while s
-    // computes
+    // computes.  The prefetch is unconditional (past the step's last
+    // sub-tile it reads absent entries, i.e. row 0): with it under a branch,
+    // the compiler's wait before the P.V products covered the prefetch too
+    // (vmcnt(0) instead of a count that leaves it in flight).
     u32x4 kst[kFp8 ? 4 : 8];
     if (n_sub > 0) load_k_quads<kFp8>(kst, tok, kc, a.Hkv, kvh);
     for (int s = 0; s < n_sub; ++s) {
@@ -692,7 +713,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs 
       int rv[4];
       load_v_rows<kFp8, false>(vr, rv, ts, vc, a.Hkv, kvh);
       store_k_tile<kFp8>(kst, k_lds);
-      if (s + 1 < n_sub) load_k_quads<kFp8>(kst, ts + 16, kc, a.Hkv, kvh);
+      load_k_quads<kFp8>(kst, ts + 16, kc, a.Hkv, kvh);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -823,7 +844,7 @@ size_t attn_smem_bytes(int stream_cap) {
   const size_t acc = sizeof(float) * (size_t)kAttnWaves * 16 * kAccPitch;
   const size_t loop = sizeof(uint16_t) * (size_t)kQLdsElems +
                       (size_t)kAttnWaves * kItemKBytesPerWave +
-                      sizeof(int32_t) * (size_t)((stream_cap + 15) / 16 * 16);
+                      sizeof(int32_t) * (size_t)((stream_cap + 15) / 16 * 16 + 16 * kAttnWaves);
   return sizeof(float) * (size_t)kMlFloats + (acc > loop ? acc : loop);
 }
 
