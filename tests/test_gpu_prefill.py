@@ -235,6 +235,19 @@ def test_prefill_kv_head_counts(gpu, hq, hkv, kv):
     _prefill_check(wl, gpu, np.arange(wl.n_q))
 
 
+@pytest.mark.parametrize("K,first_pos", [(256, 4095), (256, 4092), (255, 4095), (257, 4093)])
+def test_prefill_translation_step_edges(gpu, K, first_pos):
+    # token streams of 4K + (L mod 4) entries ending on, just before and just
+    # past a 1,024-entry translation step (the K prefetch past a step's last
+    # sub-tile then reads the step's padding entries)
+    wl = workload.prefill_workload(890 + K + first_pos % 4, first_pos, 9, kv_dtype="bf16",
+                                   topk_groups=K)
+    lens = first_pos + np.arange(wl.n_q) + 1
+    streams = 4 * K + lens % 4  # 1,020-1,031 entries over the cases
+    assert np.all((streams >= 1020) & (streams <= 1031))
+    _prefill_check(wl, gpu, np.arange(wl.n_q))
+
+
 # Prefill attention walks each query's whole selection in token order, one
 # wavefront per (query, KV head); the cases below stress the token stream:
 # few selected groups, the longest selections at full capacity, and
