@@ -79,3 +79,39 @@ def test_random_prefill(gpu, case):
     if c["bad"]:
         _break_pages(wl, c["seed"])
     _prefill_check(wl, gpu, np.arange(wl.n_q))
+
+
+# KV head counts of 3, 4 and 8 (an XCD then serves one KV head only when the
+# count divides 8): a second fixed generator, so the cases above stay as
+# they are
+HEADS_KV = [(24, 3), (16, 4), (32, 8), (48, 3), (32, 4)]
+
+
+def _kv_head_cases(n_dec=12, n_pf=8):
+    r = np.random.RandomState(20261205)
+    dec, pf = [], []
+    for i in range(n_dec):
+        hq, hkv = HEADS_KV[r.randint(len(HEADS_KV))]
+        Q = int(r.randint(1, 5))
+        while Q * (hq // hkv) > 48:
+            Q -= 1
+        lens = [int(r.randint(0, 40000)) for _ in range(int(r.randint(1, 5)))]
+        dec.append(dict(seed=8000 + i, hq=hq, hkv=hkv, Q=Q, lens=lens,
+                        K=int(BUDGETS[r.randint(len(BUDGETS))]),
+                        kv="fp8" if r.rand() < 0.5 else "bf16", bad=r.rand() < 0.3))
+    for i in range(n_pf):
+        hq, hkv = HEADS_KV[r.randint(len(HEADS_KV))]
+        pf.append(dict(seed=8500 + i, hq=hq, hkv=hkv, first=int(r.randint(0, 20000)),
+                       n_q=int(r.randint(1, 200)), K=int(BUDGETS[r.randint(len(BUDGETS))]),
+                       kv="fp8" if r.rand() < 0.5 else "bf16", bad=r.rand() < 0.3))
+    return dec, pf
+
+
+@pytest.mark.parametrize("case", _kv_head_cases()[0], ids=lambda c: f"d{c['seed']}")
+def test_random_decode_kv_heads(gpu, case):
+    test_random_decode(gpu, case)
+
+
+@pytest.mark.parametrize("case", _kv_head_cases()[1], ids=lambda c: f"p{c['seed']}")
+def test_random_prefill_kv_heads(gpu, case):
+    test_random_prefill(gpu, case)
