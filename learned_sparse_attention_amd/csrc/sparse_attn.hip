@@ -21,7 +21,11 @@
 // Waves merge their (max, sum, accumulator) through LDS, and combine_kernel
 // merges the partials of the workgroups the selection is split over.
 // Prefill: one wavefront per (query, KV head) walks the query's whole
-// selection with the same sub-tile step and writes normalised rows.
+// selection with the same sub-tile step and writes normalised rows.  The
+// wavefronts of an XCD share its L2 only while they sweep nearby tokens;
+// random selections let them drift apart, so where the expected drift is
+// large (BF16 rows, sparse selections) a wavefront that runs ahead in the
+// token space waits (pacing; timing only, the order of work is unchanged).
 //
 // V goes from HBM to registers already in MFMA operand order (16 lanes
 // read 256 contiguous bytes of one token's row).  K is loaded with
@@ -32,6 +36,9 @@
 // dimension is permuted consistently between the two MFMA operands (dot
 // products do not depend on the order of d), which is what makes those
 // contiguous loads possible.
+#include <algorithm>
+#include <cmath>
+
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
@@ -589,11 +596,34 @@ constexpr int kOutPitch = kHeadDim + 4;
 // then one sub-tile's K tile; at the end (reused) the transposed output
 // rows of the query's heads.
 constexpr int kPrefillKFloats = k_tile_bytes<false>() / 4;  // room for either element type
-constexpr int kPrefillWaveFloats = kPrefillTok + 16 + kPrefillKFloats;
+constexpr int kPrefillSubs = kPrefillTok / 16;  // sub-tiles per translation step
+#ifndef QSA_PACE_SLACK
+#define QSA_PACE_SLACK (1 << 19)
+#endif
+#ifndef QSA_PACE_GATE
+#define QSA_PACE_GATE (1 << 20)
+#endif
+#ifndef QSA_PACE_MAX_SHARE
+#define QSA_PACE_MAX_SHARE 0.05f
+#endif
+// Pacing of the prefill sweep (see attn_prefill_kernel):
+//   kPaceSlack     bytes of one KV head's K and V rows a wavefront may run
+//                  ahead of its own rate before it waits;
+//   kPaceGate      paced only if the expected spread of the wavefronts'
+//                  positions exceeds this many bytes;
+//   kPaceMaxShare  the waits of a wavefront stay under this share of its
+//                  working time.
+constexpr int kPaceSlack = QSA_PACE_SLACK;
+constexpr int kPaceGate = QSA_PACE_GATE;
+constexpr float kPaceMaxShare = QSA_PACE_MAX_SHARE;
+// K and V bytes of one group (4 tokens) of one KV head
+template <bool kFp8>
+constexpr int kPaceGroupBytes() { return 2 * kRatio * kHeadDim * (kFp8 ? 1 : 2); }
+constexpr int kPrefillWaveFloats = kPrefillTok + 16 + kPrefillKFloats + kPrefillSubs;
 constexpr int kOutRowsLds = kPrefillWaveFloats / kOutPitch;  // output rows per LDS pass
 static_assert(kOutRowsLds >= 8, "a pass holds at least 8 output rows");
 
-template <bool kFp8>
+template <bool kFp8, bool kPace>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs a, int n_qb) {
   extern __shared__ float smem[];
   const int gq = a.Hq / a.Hkv;
@@ -618,6 +648,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs 
   float* wl = smem + (size_t)wave * kPrefillWaveFloats;
   int32_t* tok = reinterpret_cast<int32_t*>(wl);
   uint8_t* k_lds = reinterpret_cast<uint8_t*>(wl + kPrefillTok + 16);
+  // group id of each sub-tile's first selected group in the current step
+  int32_t* sgid = reinterpret_cast<int32_t*>(wl + kPrefillTok + 16 + kPrefillKFloats);
   // the 16 entries past a translation step: absent, so the K prefetch past
   // a step's last sub-tile reads row 0 (the translation writes the rest)
   if (lane < 16) tok[kPrefillTok + lane] = -1;
@@ -651,6 +683,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs 
   const uint8_t* vc = reinterpret_cast<const uint8_t*>(a.v);
   const int32_t* pt = a.page_table + (size_t)a.req * a.max_pages;
   const int32_t* srow = a.sel + (size_t)q * a.K;
+  const uint64_t t0 = kPace ? __builtin_amdgcn_s_memrealtime() : 0;
+  uint64_t waited = 0;  // pacing waits so far
+  const float slack_groups = (float)kPaceSlack / (float)kPaceGroupBytes<kFp8>();
 
   for (int c0 = 0; c0 < n_stream; c0 += kPrefillTok) {
     // stream entries c0 + 4*(u*64 + lane) .. + 3 -> physical rows: a selected
@@ -666,6 +701,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs 
       }
 #pragma unroll
       for (int u = 0; u < kPrefillGpl; ++u) ph[u] = gs[u] >= 0 ? pt[(kRatio * gs[u]) / kPage] : -1;
+      if (kPace) {
+#pragma unroll
+        for (int u = 0; u < kPrefillGpl; ++u)
+          if ((lane & 3) == 0) sgid[u * (kWave / 4) + lane / 4] = gs[u];
+      }
 #pragma unroll
       for (int u = 0; u < kPrefillGpl; ++u) {
         const int e = c0 + kRatio * (u * kWave + lane);
@@ -708,6 +748,37 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs 
     if (n_sub > 0) load_k_quads<kFp8>(kst, tok, kc, a.Hkv, kvh);
     for (int s = 0; s < n_sub; ++s) {
       const int32_t* ts = tok + 16 * s;
+      // pacing: a wavefront whose position in the token space (group id over
+      // G) runs ahead of its share of the work (selection index over
+      // n_groups) waits until its own average rate catches up, so that the
+      // wavefronts of an XCD sweep the cache together
+      if (kPace && (s & 3) == 0) {
+        const int j = (c0 + 16 * s) / kRatio;
+        if (j >= 64 && j < n_groups) {
+          const int gid = __builtin_amdgcn_readfirstlane(sgid[s]);
+          // position fraction less the slack a wavefront may run ahead
+          // (kPaceSlack bytes of one KV head's K and V rows)
+          const float x = ((float)gid - slack_groups) * __builtin_amdgcn_rcpf((float)G);
+          const float lead = x * (float)n_groups * __builtin_amdgcn_rcpf((float)j) - 1.0f;
+          if (lead > 0.0f) {
+            // work time so far (elapsed minus earlier waits) sets the
+            // wavefront's own rate; the wait brings its position and its
+            // elapsed time back into that ratio, less what it already waited
+            const uint64_t now = __builtin_amdgcn_s_memrealtime();
+            const float work = (float)(now - t0 - waited);
+            const float w = fminf(lead, kPaceMaxShare) * work - (float)waited;
+            if (w > 0.0f) {
+              const uint64_t until = now + (uint64_t)w;
+              uint64_t t = now;
+              while (t < until) {
+                __builtin_amdgcn_s_sleep(2);
+                t = __builtin_amdgcn_s_memrealtime();
+              }
+              waited += t - now;
+            }
+          }
+        }
+      }
       // V rows in operand order
       u32x4 vr[4][kFp8 ? 1 : 2];
       int rv[4];
@@ -865,7 +936,7 @@ hipError_t launch_decode_t(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool kFp8>
+template <bool kFp8, bool kPace>
 hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
   if (a.Hq / a.Hkv > 16) return hipErrorInvalidValue;
   const int n_qb = (a.batch + kAttnWaves - 1) / kAttnWaves;
@@ -875,7 +946,7 @@ hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
     n_wg = (size_t)((n_qb + nx - 1) / nx) * kXcds;
   }
   const size_t smem = sizeof(float) * (size_t)kAttnWaves * kPrefillWaveFloats;
-  hipLaunchKernelGGL((attn_prefill_kernel<kFp8>), dim3((unsigned)n_wg), dim3(kAttnThreads), smem,
+  hipLaunchKernelGGL((attn_prefill_kernel<kFp8, kPace>), dim3((unsigned)n_wg), dim3(kAttnThreads), smem,
                      stream, a, n_qb);
   return hipGetLastError();
 }
@@ -883,10 +954,25 @@ hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
 // One 16-row block per workgroup: query rows beyond 16 (e.g. 12 heads x 3
 // draft positions) take further workgroups over the same tokens, which
 // then mostly come from the caches.
+// Whether a prefill chunk's sweep is paced.  With n groups drawn evenly at
+// random from G, the position of a wavefront's middle group varies by about
+// G / (2 sqrt(n)) groups; the chunk is paced when twice that, in bytes of one
+// KV head's K and V, exceeds kPaceGate (and each query keeps >= 128 groups).
+bool prefill_paced(const AttnArgs& a) {
+  const double G = (double)(a.first_pos + a.batch) / kRatio;
+  const double n = std::min((double)a.K, G);
+  if (n < 128) return false;
+  const int gb = a.kv_dtype == 1 ? kPaceGroupBytes<true>() : kPaceGroupBytes<false>();
+  return G / std::sqrt(n) * gb > (double)kPaceGate;
+}
+
 hipError_t dispatch(const AttnArgs& a, hipStream_t stream, bool prefill) {
+  if (!prefill)
+    return a.kv_dtype == 1 ? launch_decode_t<true>(a, stream) : launch_decode_t<false>(a, stream);
+  const bool pace = prefill_paced(a);
   if (a.kv_dtype == 1)
-    return prefill ? launch_prefill_t<true>(a, stream) : launch_decode_t<true>(a, stream);
-  return prefill ? launch_prefill_t<false>(a, stream) : launch_decode_t<false>(a, stream);
+    return pace ? launch_prefill_t<true, true>(a, stream) : launch_prefill_t<true, false>(a, stream);
+  return pace ? launch_prefill_t<false, true>(a, stream) : launch_prefill_t<false, false>(a, stream);
 }
 
 }  // namespace
