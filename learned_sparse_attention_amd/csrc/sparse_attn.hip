@@ -593,19 +593,11 @@ constexpr int kPrefillGpl = kPrefillTok / (kRatio * kWave);  // groups per lane 
 // banks)
 constexpr int kOutPitch = kHeadDim + 4;
 // LDS per wavefront, in floats: the token rows of one translation step,
-// then one sub-tile's K tile; at the end (reused) the transposed output
+// then one sub-tile's K tile, then (paced sweeps) the group id that each
+// sub-tile of the step starts at; at the end (reused) the transposed output
 // rows of the query's heads.
 constexpr int kPrefillKFloats = k_tile_bytes<false>() / 4;  // room for either element type
 constexpr int kPrefillSubs = kPrefillTok / 16;  // sub-tiles per translation step
-#ifndef QSA_PACE_SLACK
-#define QSA_PACE_SLACK (1 << 19)
-#endif
-#ifndef QSA_PACE_GATE
-#define QSA_PACE_GATE (1 << 20)
-#endif
-#ifndef QSA_PACE_MAX_SHARE
-#define QSA_PACE_MAX_SHARE 0.05f
-#endif
 // Pacing of the prefill sweep (see attn_prefill_kernel):
 //   kPaceSlack     bytes of one KV head's K and V rows a wavefront may run
 //                  ahead of its own rate before it waits;
@@ -613,9 +605,9 @@ constexpr int kPrefillSubs = kPrefillTok / 16;  // sub-tiles per translation ste
 //                  positions exceeds this many bytes;
 //   kPaceMaxShare  the waits of a wavefront stay under this share of its
 //                  working time.
-constexpr int kPaceSlack = QSA_PACE_SLACK;
-constexpr int kPaceGate = QSA_PACE_GATE;
-constexpr float kPaceMaxShare = QSA_PACE_MAX_SHARE;
+constexpr int kPaceSlack = 1 << 19;
+constexpr int kPaceGate = 1 << 20;
+constexpr float kPaceMaxShare = 0.05f;
 // K and V bytes of one group (4 tokens) of one KV head
 template <bool kFp8>
 constexpr int kPaceGroupBytes() { return 2 * kRatio * kHeadDim * (kFp8 ? 1 : 2); }
