@@ -277,3 +277,28 @@ def test_prefill_selection_in_one_region(gpu):
         wl.khat[wl.page_table[0, g // 16], g % 16] = 4.0 * wl.q_idx[0]
     _, gg = _prefill_check(wl, gpu, np.arange(wl.n_q))
     assert np.all((gg >= 16384 // 4) & (gg < 24576 // 4))
+
+
+def _paced_regime(wl):
+    # the library paces a BF16 or FP8 chunk's sweep when G / sqrt(n) groups
+    # of one KV head's K and V (4 tokens x 256 dims x 2 for K and V, x2
+    # bytes for BF16) exceed 1 MiB and every query keeps n >= 128 groups
+    G = (wl.first_pos + wl.n_q) / 4
+    n = min(wl.geom["topk_groups"], G)
+    gb = 2 * 4 * 256 * (1 if wl.geom["kv_dtype"] == 1 else 2)
+    return n >= 128 and G / np.sqrt(n) * gb > (1 << 20)
+
+
+def test_prefill_paced_sweep_every_row(gpu):
+    # a BF16 chunk in the paced regime with a ragged query count: scores,
+    # top-K and attention on every row, then a second call bitwise equal
+    # (the waits change timing only)
+    import torch
+    wl = workload.prefill_workload(861, 16384, 203, kv_dtype="bf16", topk_groups=128)
+    assert _paced_regime(wl)
+    _prefill_check(wl, gpu, np.arange(wl.n_q))
+    d = H.to_dev(wl, gpu)
+    a = H.run_prefill(wl, d)["out"].clone()
+    b = H.run_prefill(wl, d)["out"]
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
