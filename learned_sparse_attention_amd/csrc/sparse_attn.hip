@@ -760,9 +760,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs 
             const float work = (float)(now - t0 - waited);
             const float w = fminf(lead, kPaceMaxShare) * work - (float)waited;
             if (w > 0.0f) {
+              // the real-time counter runs at 100 MHz; the spin is also
+              // bounded by a count of sleeps (each >= 128 clocks), so it
+              // ends even if the counter stood still
               const uint64_t until = now + (uint64_t)w;
               uint64_t t = now;
-              while (t < until) {
+              for (int spins = 0; t < until && spins < (1 << 16); ++spins) {
                 __builtin_amdgcn_s_sleep(2);
                 t = __builtin_amdgcn_s_memrealtime();
               }
