@@ -3,8 +3,8 @@ launch configuration bench.py times (qsa_decode / qsa_prefill with their
 default splits): scores, exact top-K (tie window 1e-6 of the K-th score),
 token lists (bit-exact) and attention on the GPU's own selection.  The
 decode workloads are checked on every request.  The long-prefill chunk is
-checked in test_gpu_prefill.py (test_prefill_long_chunk_every_row): scores
-and top-K on every one of its 4,096 query rows, attention on sampled rows."""
+checked in test_gpu_prefill.py (test_prefill_long_chunk_every_row): scores,
+top-K and attention on every one of its 4,096 query rows."""
 import numpy as np
 import pytest
 
