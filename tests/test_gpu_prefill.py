@@ -303,3 +303,17 @@ def test_prefill_paced_sweep_every_row(gpu):
     b = H.run_prefill(wl, d)["out"]
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("hq,hkv,kv", [(24, 3, "bf16"), (12, 1, "bf16"), (16, 2, "fp8")])
+def test_prefill_paced_sweep_head_layouts(gpu, hq, hkv, kv):
+    # the paced sweep with 3 KV heads (the workgroups take the plain order,
+    # 8 XCDs not being a multiple of 3), with 12 query heads on one KV head,
+    # and over an FP8 cache (its rows are half the bytes, so it needs a
+    # longer context to reach the paced regime); every row checked
+    n_q = 77
+    first_pos = 16384 if kv == "bf16" else 65536
+    wl = workload.prefill_workload(870 + hq + hkv, first_pos, n_q, num_q_heads=hq,
+                                   num_kv_heads=hkv, kv_dtype=kv, topk_groups=128)
+    assert _paced_regime(wl)
+    _prefill_check(wl, gpu, np.arange(wl.n_q))
