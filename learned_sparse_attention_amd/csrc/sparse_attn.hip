@@ -691,20 +691,29 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs 
   uint64_t waited = 0;  // pacing waits so far
   const float slack_groups = (float)kPaceSlack / (float)kPaceGroupBytes<kFp8>();
 
+  // the group ids and page ids of a translation step's selected entries:
+  // those of the first step are loaded here, those of each next step while
+  // the current step's sub-tiles compute (group ids at its start, page ids
+  // from its kPhAt-th sub-tile on), so only the first step waits for them
+  int gs[kPrefillGpl], ph[kPrefillGpl];
+  auto load_gs = [&](int c) {
+#pragma unroll
+    for (int u = 0; u < kPrefillGpl; ++u) {
+      const int e = c + kRatio * (u * kWave + lane);
+      gs[u] = e < kRatio * n_groups ? srow[e / kRatio] : -1;
+    }
+  };
+  auto load_ph = [&]() {
+#pragma unroll
+    for (int u = 0; u < kPrefillGpl; ++u) ph[u] = gs[u] >= 0 ? pt[(kRatio * gs[u]) / kPage] : -1;
+  };
+  constexpr int kPhAt = 8;
+  load_gs(0);
+  load_ph();
   for (int c0 = 0; c0 < n_stream; c0 += kPrefillTok) {
     // stream entries c0 + 4*(u*64 + lane) .. + 3 -> physical rows: a selected
     // group's four tokens (one page), or up to four current-block tokens.
-    // All of a lane's selection loads are issued before its page-table
-    // loads, so a step costs two memory round trips.
     {
-      int gs[kPrefillGpl], ph[kPrefillGpl];
-#pragma unroll
-      for (int u = 0; u < kPrefillGpl; ++u) {
-        const int e = c0 + kRatio * (u * kWave + lane);
-        gs[u] = e < kRatio * n_groups ? srow[e / kRatio] : -1;
-      }
-#pragma unroll
-      for (int u = 0; u < kPrefillGpl; ++u) ph[u] = gs[u] >= 0 ? pt[(kRatio * gs[u]) / kPage] : -1;
       if (kPace) {
 #pragma unroll
         for (int u = 0; u < kPrefillGpl; ++u)
@@ -736,6 +745,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs 
         *reinterpret_cast<int4*>(tok + kRatio * (u * kWave + lane)) = rr;
       }
     }
+    const bool has_next = c0 + kPrefillTok < n_stream;
+    if (has_next) load_gs(c0 + kPrefillTok);
     // LDS operations of one wavefront execute in order; the fences keep the
     // compiler from moving the reads below above the writes
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -752,6 +763,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_prefill_kernel(AttnArgs 
     if (n_sub > 0) load_k_quads<kFp8>(kst, tok, kc, a.Hkv, kvh);
     for (int s = 0; s < n_sub; ++s) {
       const int32_t* ts = tok + 16 * s;
+      if (s == kPhAt && has_next) load_ph();  // a step with a next one is full
       // pacing: a wavefront whose position in the token space (group id over
       // G) runs ahead of its share of the work (selection index over
       // n_groups) waits until its own average rate catches up, so that the
