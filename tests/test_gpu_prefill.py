@@ -135,12 +135,12 @@ def test_prefill_long_chunk_every_row(gpu):
 def test_prefill_long_7810_queries_over_65536(gpu):
     # the operator suite's long-prefill case (PR #41855 article, Tests):
     # 7,810 queries ending a 65,536-token cache, 2,051 selected slots each
-    # (K = 512 groups plus the current block).  Scores and top-K on every
-    # row; attention on sampled rows, as the article's test samples rows.
+    # (K = 512 groups plus the current block).  Scores, top-K and attention
+    # on every row (the article's own test samples rows for the attention).
     # The score rows are 16,384 groups long: the 512-thread row kernel.
     wl = workload.prefill_workload(830, 65536 - 7810, 7810, kv_dtype="bf16", topk_groups=512)
     assert 4 * wl.geom["topk_groups"] + 3 == 2051 and wl.gstride == 16384
-    _prefill_check(wl, gpu, _sample_rows(wl.n_q, 5))
+    _prefill_check(wl, gpu, np.arange(wl.n_q))
 
 
 # Score rows longer than 16,384 groups (prefill past 65,536 tokens, up to
