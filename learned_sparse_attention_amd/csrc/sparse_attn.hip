@@ -970,9 +970,6 @@ hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// One 16-row block per workgroup: query rows beyond 16 (e.g. 12 heads x 3
-// draft positions) take further workgroups over the same tokens, which
-// then mostly come from the caches.
 // Whether a prefill chunk's sweep is paced.  With n groups drawn evenly at
 // random from G, the position of a wavefront's middle group varies by about
 // G / (2 sqrt(n)) groups; the chunk is paced when twice that, in bytes of one
@@ -985,6 +982,9 @@ bool prefill_paced(const AttnArgs& a) {
   return G / std::sqrt(n) * gb > (double)kPaceGate;
 }
 
+// One 16-row block per workgroup: query rows beyond 16 (e.g. 12 heads x 3
+// draft positions) take further workgroups over the same tokens, which
+// then mostly come from the caches.
 hipError_t dispatch(const AttnArgs& a, hipStream_t stream, bool prefill) {
   if (!prefill)
     return a.kv_dtype == 1 ? launch_decode_t<true>(a, stream) : launch_decode_t<false>(a, stream);
