@@ -617,7 +617,7 @@ constexpr int kPrefillSubs = kPrefillTok / 16;  // sub-tiles per translation ste
 //                  positions exceeds this many bytes;
 //   kPaceMaxShare  the waits of a wavefront stay under this share of its
 //                  working time.
-constexpr int kPaceSlack = 1 << 19;
+constexpr int kPaceSlack = 1 << 18;
 constexpr int kPaceGate = 1 << 20;
 constexpr float kPaceMaxShare = 0.05f;
 // K and V bytes of one group (4 tokens) of one KV head
